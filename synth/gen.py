@@ -1,0 +1,241 @@
+"""Seeded instance generation (NumPy Philox streams, host memory).
+
+Recipe (one instance per (spec, seed)):
+
+* ``SeedSequence([cfg_id, seed]).spawn(6)`` gives six independent Philox streams:
+  tree shape, tree-token Q/K/V, KV cache, logits, draft draws, uniforms.
+* Tree: nodes at depth d+1 take a parent drawn uniformly from the depth-d nodes;
+  nodes are numbered by depth, then parent, then draw order, so ``parent[i] < i``
+  and siblings are contiguous in the order they were drafted.
+* Logits: draft logits ``z_q ~ N(0, draft_std^2)`` per (sequence, node, token);
+  target logits ``z_p = z_q + N(0, sigma^2)``, stored in ``logit_dtype``.
+* Draft distribution (synthetic drafter): ``q = softmax(z_q / tau)`` in float64,
+  stored float32; for a greedy sequence (tau = 0) the row holds softmax(z_q).
+* Draft tokens: a node's children are drawn one after another from the stored
+  q row of that node, without replacement ("wor") or i.i.d. ("iid"); for a
+  greedy sequence they are the top-k of z_q (ties to the lowest index).  The root
+  token is uniform over the vocabulary.
+* Attention inputs q, k_new, v_new, k_cache, v_cache ~ N(0, 1), cast to ``dtype``.
+* Uniforms ``u_accept``, ``u_sample`` ~ U[0, 1) float32.
+
+Padding rows (node index >= T_b) are filled too (random values, parent -1,
+token 0); correct consumers never read them.
+"""
+from dataclasses import dataclass, field
+import numpy as np
+
+
+def bf16_bits_from_f32(x):
+    """Round float32 to bfloat16 (nearest-even); returns the uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in = x.reshape(-1)
+    flat_out = out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat_in.size, step):
+        u = flat_in[s:s + step].view(np.uint32)
+        r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+        flat_out[s:s + step] = r.astype(np.uint16)
+    return out
+
+
+def f32_from_bf16_bits(b):
+    """Widen bfloat16 bit patterns (uint16) to float32 exactly."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Instance:
+    spec: dict
+    B: int
+    T_max: int
+    V: int
+    Hq: int
+    Hkv: int
+    D: int
+    L_max: int
+    dtype: str
+    logit_dtype: str
+    sibling_mode: str
+    parent: np.ndarray          # [B][T_max] int32
+    num_nodes: np.ndarray       # [B] int32
+    tokens: np.ndarray          # [B][T_max] int32
+    prefix_len: np.ndarray      # [B] int32
+    temperature: np.ndarray     # [B] float32
+    q: np.ndarray = None        # [B][T_max][Hq][D]  (uint16 bf16 bits or float32)
+    k_new: np.ndarray = None    # [B][T_max][Hkv][D]
+    v_new: np.ndarray = None    # [B][T_max][Hkv][D]
+    k_cache: np.ndarray = None  # [B][Hkv][L_max][D]
+    v_cache: np.ndarray = None  # [B][Hkv][L_max][D]
+    target_logits: np.ndarray = None  # [B][T_max][V] (uint16 bf16 bits or float32)
+    q_probs: np.ndarray = None  # [B][T_max][V] float32
+    u_accept: np.ndarray = None  # [B][T_max] float32
+    u_sample: np.ndarray = None  # [B][T_max] float32
+    extra: dict = field(default_factory=dict)
+
+
+def tree_from_widths(widths, rng):
+    """Parent array (root at 0) of a tree with ``widths[d]`` nodes at depth d+1.
+
+    Each depth-(d+1) node picks its parent uniformly among the depth-d nodes;
+    nodes are then numbered by depth, then parent index, then draw order.
+    """
+    parent = [-1]
+    prev = [0]
+    for w in widths:
+        picks = rng.integers(0, len(prev), size=int(w))
+        order = np.argsort(picks, kind="stable")
+        cur = []
+        for j in order:
+            cur.append(len(parent))
+            parent.append(prev[int(picks[j])])
+        prev = cur
+    return np.asarray(parent, dtype=np.int32)
+
+
+def random_tree_widths(rng, depth_lo, depth_hi, width_lo, width_hi, n_lo, n_hi):
+    """Per-depth widths drawn uniformly, resampled until the node count fits."""
+    for _ in range(100000):
+        depth = int(rng.integers(depth_lo, depth_hi + 1))
+        widths = rng.integers(width_lo, width_hi + 1, size=depth)
+        if n_lo <= int(widths.sum()) <= n_hi:
+            return [int(w) for w in widths]
+    raise RuntimeError("could not draw a tree of the requested size")
+
+
+def _normal(rng, shape, std, out_dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if out_dtype == "bf16":
+        return bf16_bits_from_f32(x)
+    return x
+
+
+def _per_seq(value, B, rng):
+    if isinstance(value, (list, np.ndarray)):
+        assert len(value) == B
+        return list(value)
+    if isinstance(value, tuple) and value[0] == "choice":
+        opts = value[1]
+        return [opts[int(i)] for i in rng.integers(0, len(opts), size=B)]
+    return [value] * B
+
+
+def _draw_children(qrow64, k, mode, rng):
+    """k draft tokens from one q row (inverse CDF on the float64 row)."""
+    w = qrow64.copy()
+    out = []
+    for _ in range(k):
+        c = np.cumsum(w)
+        u = rng.random()
+        y = int(np.searchsorted(c, u * c[-1], side="right"))
+        y = min(y, w.size - 1)
+        while w[y] <= 0.0 and y > 0:   # never land on a zero-mass token
+            y -= 1
+        out.append(y)
+        if mode == "wor":
+            w[y] = 0.0
+    return out
+
+
+def make_instance(spec, seed=0, with_attn=True, with_accept=True):
+    """Build one seeded instance of ``spec`` (see :mod:`synth.configs`)."""
+    s = dict(spec)
+    B, Hq, Hkv, D, V = s["B"], s["Hq"], s["Hkv"], s["D"], s["V"]
+    cfg_id = int(s.get("cfg_id", 0))
+    ss = np.random.SeedSequence([cfg_id, int(seed)])
+    r_tree, r_qkv, r_cache, r_logits, r_draft, r_unif = [
+        np.random.Generator(np.random.Philox(c)) for c in ss.spawn(6)]
+
+    # ---- tree shapes
+    kind = s["tree"][0]
+    parents = []
+    for b in range(B):
+        if kind == "widths":
+            parents.append(tree_from_widths(s["tree"][1], r_tree))
+        elif kind == "chain":
+            n = int(s["tree"][1])
+            parents.append(np.arange(-1, n, dtype=np.int32))
+        elif kind == "dynamic":
+            widths = random_tree_widths(r_tree, *s["tree"][1:])
+            parents.append(tree_from_widths(widths, r_tree))
+        elif kind == "explicit":
+            parents.append(np.asarray(s["tree"][1][b], dtype=np.int32))
+        else:
+            raise ValueError(kind)
+    num_nodes = np.array([len(p) for p in parents], dtype=np.int32)
+    T_max = int(s.get("T_max", num_nodes.max()))
+    assert T_max >= num_nodes.max()
+    parent = np.full((B, T_max), -1, dtype=np.int32)
+    for b, p in enumerate(parents):
+        parent[b, :len(p)] = p
+
+    taus = np.asarray(_per_seq(s["tau"], B, r_tree), dtype=np.float32)
+    pl = s["prefix_len"]
+    prefix_len = np.asarray(pl if isinstance(pl, (list, tuple, np.ndarray)) else [pl] * B,
+                            dtype=np.int32)
+    L_max = int(s.get("L_max", max(1, int(prefix_len.max()))))
+    dtype = s["dtype"]
+    logit_dtype = s["logit_dtype"]
+    mode = s.get("sibling_mode", "wor")
+
+    inst = Instance(spec=s, B=B, T_max=T_max, V=V, Hq=Hq, Hkv=Hkv, D=D, L_max=L_max,
+                    dtype=dtype, logit_dtype=logit_dtype, sibling_mode=mode,
+                    parent=parent, num_nodes=num_nodes,
+                    tokens=np.zeros((B, T_max), dtype=np.int32),
+                    prefix_len=prefix_len, temperature=taus)
+
+    # ---- attention inputs
+    if with_attn:
+        inst.q = _normal(r_qkv, (B, T_max, Hq, D), 1.0, dtype)
+        inst.k_new = _normal(r_qkv, (B, T_max, Hkv, D), 1.0, dtype)
+        inst.v_new = _normal(r_qkv, (B, T_max, Hkv, D), 1.0, dtype)
+        inst.k_cache = np.empty((B, Hkv, L_max, D), dtype=np.uint16 if dtype == "bf16" else np.float32)
+        inst.v_cache = np.empty_like(inst.k_cache)
+        for b in range(B):
+            inst.k_cache[b] = _normal(r_cache, (Hkv, L_max, D), 1.0, dtype)
+            inst.v_cache[b] = _normal(r_cache, (Hkv, L_max, D), 1.0, dtype)
+
+    # ---- logits, draft distribution, draft tokens, uniforms
+    draft_std = float(s.get("draft_std", 3.0))
+    sigma = float(s.get("sigma", 1.0))
+    tokens = np.zeros((B, T_max), dtype=np.int32)
+    if with_accept:
+        inst.target_logits = np.empty((B, T_max, V),
+                                      dtype=np.uint16 if logit_dtype == "bf16" else np.float32)
+        inst.q_probs = np.empty((B, T_max, V), dtype=np.float32)
+    for b in range(B):
+        zq = r_logits.standard_normal(size=(T_max, V), dtype=np.float32) * np.float32(draft_std)
+        noise = r_logits.standard_normal(size=(T_max, V), dtype=np.float32) * np.float32(sigma)
+        zp = zq + noise
+        del noise
+        tau = float(taus[b])
+        t_eff = tau if tau > 0 else 1.0
+        z64 = zq.astype(np.float64) / t_eff
+        z64 -= z64.max(axis=1, keepdims=True)
+        np.exp(z64, out=z64)
+        z64 /= z64.sum(axis=1, keepdims=True)
+        q32 = z64.astype(np.float32)
+        del z64
+        if with_accept:
+            inst.target_logits[b] = bf16_bits_from_f32(zp) if logit_dtype == "bf16" else zp
+            inst.q_probs[b] = q32
+        # draft tokens
+        Tb = int(num_nodes[b])
+        tokens[b, 0] = int(r_draft.integers(0, V))
+        par = parent[b, :Tb]
+        for n in range(Tb):
+            kids = np.nonzero(par == n)[0]
+            if kids.size == 0:
+                continue
+            if tau > 0:
+                drawn = _draw_children(q32[n].astype(np.float64), kids.size, mode, r_draft)
+            else:
+                drawn = [int(i) for i in np.argsort(-zq[n], kind="stable")[:kids.size]]
+            tokens[b, kids] = drawn
+    inst.tokens = tokens
+    inst.u_accept = r_unif.random(size=(B, T_max), dtype=np.float32)
+    inst.u_sample = r_unif.random(size=(B, T_max), dtype=np.float32)
+    return inst
