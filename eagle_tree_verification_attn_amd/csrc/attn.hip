@@ -1,0 +1,722 @@
+// Tree attention for verification: every tree position attends to its
+// sequence's KV-cache prefix and to its own tree ancestors (and itself).
+//
+// [EAGLE article] sec. 1.3 "Verification": the target scores the whole draft
+// tree in one forward pass using tree attention.  [Spec-decoding lesson]
+// "Tree-attention verification": one forward, one matmul; the topology mask
+// only adds a few KV entries.
+//
+// bf16 kernel (gfx950 MFMA).  Work unit = (sequence b, KV head, block of query
+// rows, range of keys).  Query rows of one KV head are the (node t, head g)
+// pairs, row r = t * G + g, so the G heads sharing a KV head are packed into
+// the MFMA N dimension next to each other.  Per wave, NT tiles of 16 rows;
+// per workgroup, NW waves share each key block staged in LDS.
+//
+//   scores   S^T[key][row] = K[key] . Q[row]     v_mfma_f32_16x16x32_bf16,
+//            A = K rows from LDS, B = Q held in registers for the whole run;
+//   softmax  online, fp32, exp2 with the scale folded in; the running max is
+//            only raised when a block's max exceeds it by more than 8 (log2
+//            units), so the O rescale is rare and exp2 arguments stay <= 8;
+//   output   O^T[d][row] += V^T[d][key] P^T[key][row], A = V^T from LDS (V is
+//            transposed on its way into LDS), B = P taken straight from the
+//            score registers (same key permutation on both operands).
+//
+// Keys of one (b, KV head) are numbered 0 .. L_b + T_b - 1: first the cache
+// prefix, then the tree tokens; keys >= L_b are visible to row (t, g) iff bit
+// (key - L_b) of anc[b][t] is set.  With several key ranges per row
+// (lsplit > 1), each range writes (m, l, O) partials and k_attn_combine merges
+// them with the log-sum-exp rule.
+#include "sv_internal.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+namespace sv {
+
+constexpr int BK = 32;  // keys per block
+
+struct AttnParams {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* prefix_len;
+  const int32_t* num_nodes;
+  const int32_t* status;
+  const uint64_t* anc;
+  void* out;
+  float* part_o;   // [B][T_max][Hq][lsplit][D]
+  float* part_ml;  // [B][T_max][Hq][lsplit][2]
+  int B, T_max, Hq, Hkv, G, L_max, W;
+  int rows_per_wg, msplit, lsplit, chunk;
+  int remap;
+  float scale_log2;
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (block i runs on XCD
+// i % 8).  With remap set (grid a multiple of 8) consecutive logical blocks --
+// the row blocks that read the same keys -- are placed on the same XCD, one
+// after another, so their shared K/V tiles are served from that XCD's L2.
+__device__ inline int logical_block(int remap) {
+  const int i = blockIdx.x;
+  if (!remap) return i;
+  const int per = gridDim.x >> 3;
+  return (i & 7) * per + (i >> 3);
+}
+
+__device__ inline float wave_max16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ inline float wave_sum16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <int D, int NT, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_bf16(AttnParams p) {
+  constexpr int NTHR = NW * 64;
+  constexpr int KS = D + 8;    // LDS row stride (elements) of the K tile  [BK][KS]
+  constexpr int VS = BK + 4;   // LDS row stride (elements) of the V^T tile [D][VS]
+  constexpr int K_ELEMS = BK * KS;
+  constexpr int V_ELEMS = D * VS;
+  constexpr int STAGE = K_ELEMS + V_ELEMS;
+  constexpr int KCH = BK * D / 8;         // 16-byte K chunks per block
+  constexpr int VUN = (BK / 2) * (D / 8); // V units (2 keys x 8 dims) per block
+  constexpr int KPT = (KCH + NTHR - 1) / NTHR;
+  constexpr int VPT = (VUN + NTHR - 1) / NTHR;
+  constexpr int DK = D / 32;              // MFMA k-steps over the head dim
+  constexpr int DT = D / 16;              // 16-row output tiles over the head dim
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+  uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem_raw + 2 * STAGE * sizeof(__bf16));
+
+  const int lb = logical_block(p.remap);
+  const int ms_i = lb % p.msplit;
+  const int rest = lb / p.msplit;
+  const int ls_i = rest % p.lsplit;
+  const int unit = rest / p.lsplit;
+  const int b = unit / p.Hkv;
+  const int kvh = unit % p.Hkv;
+  const int G = p.G;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = lane & 15;   // column (query row) within a 16x16 tile
+  const int g = lane >> 4;   // lane group
+
+  const int Tb = p.num_nodes[b];
+  const int Lb = p.prefix_len[b];
+  // a sequence whose tree is invalid, or whose sizes are out of range, is
+  // written as zeros
+  const bool seq_ok = p.status[b] == SV_TREE_OK && Tb >= 1 && Tb <= p.T_max && Lb >= 0 && Lb <= p.L_max;
+  const int row0 = ms_i * p.rows_per_wg;
+  const int valid_rows = seq_ok ? Tb * G : 0;
+  const int kbeg = ls_i * p.chunk;
+  const int kend = min(kbeg + p.chunk, Lb + Tb);
+
+  const __bf16* qp = reinterpret_cast<const __bf16*>(p.q);
+  const __bf16* kc = reinterpret_cast<const __bf16*>(p.k_cache) + ((size_t)b * p.Hkv + kvh) * p.L_max * D;
+  const __bf16* vc = reinterpret_cast<const __bf16*>(p.v_cache) + ((size_t)b * p.Hkv + kvh) * p.L_max * D;
+  const __bf16* kn = reinterpret_cast<const __bf16*>(p.k_new) + ((size_t)b * p.T_max * p.Hkv + kvh) * D;
+  const __bf16* vn = reinterpret_cast<const __bf16*>(p.v_new) + ((size_t)b * p.T_max * p.Hkv + kvh) * D;
+  const size_t new_stride = (size_t)p.Hkv * D;  // elements between consecutive tree tokens
+
+  // rows owned by this lane (one per 16-row tile)
+  int rrow[NT];
+  bool rvalid[NT];
+#pragma unroll
+  for (int qt = 0; qt < NT; ++qt) {
+    rrow[qt] = row0 + (wave * NT + qt) * 16 + c;
+    rvalid[qt] = rrow[qt] < valid_rows;
+  }
+
+  if (row0 >= valid_rows || kbeg >= kend) {
+    // Nothing to attend for this workgroup: write zeros (single range) or an
+    // empty partial (m = -inf, l = 0, O = 0).
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+      const int r = rrow[qt];
+      if (r >= p.T_max * G) continue;
+      const int t = r / G, h = kvh * G + r % G;
+      const size_t orow = ((size_t)b * p.T_max + t) * p.Hq + h;
+      if (p.lsplit == 1) {
+        __bf16* o = reinterpret_cast<__bf16*>(p.out) + orow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<uint2*>(o + dt * 16 + 4 * g) = make_uint2(0u, 0u);
+      } else if (rvalid[qt]) {
+        float* po = p.part_o + (orow * p.lsplit + ls_i) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (g == 0) {
+          float* pm = p.part_ml + (orow * p.lsplit + ls_i) * 2;
+          pm[0] = -INFINITY;
+          pm[1] = 0.f;
+        }
+      }
+    }
+    return;
+  }
+
+  // ancestor rows of this sequence -> LDS
+  const int W = p.W;
+  for (int i = tid; i < p.T_max * W; i += NTHR) anc_s[i] = p.anc[(size_t)b * p.T_max * W + i];
+
+  // queries -> registers (B operand of the score MFMA)
+  bf16x8 qreg[NT][DK];
+#pragma unroll
+  for (int qt = 0; qt < NT; ++qt) {
+    const int r = rrow[qt];
+    if (rvalid[qt]) {
+      const int t = r / G, h = kvh * G + r % G;
+      const __bf16* src = qp + (((size_t)b * p.T_max + t) * p.Hq + h) * D + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) qreg[qt][kk] = *reinterpret_cast<const bf16x8*>(src + 32 * kk);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) qreg[qt][kk] = bf16x8{};
+    }
+  }
+
+  f32x4 acc[NT][DT];
+  float m_run[NT], l_part[NT];
+#pragma unroll
+  for (int qt = 0; qt < NT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_part[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- staging of one key block: global -> registers -> LDS
+  uint4 kst[KPT];
+  uint4 vst[VPT][2];
+  auto key_src = [&](int j, const __bf16* cache, const __bf16* tree) -> const __bf16* {
+    return j < Lb ? cache + (size_t)j * D : tree + (size_t)(j - Lb) * new_stride;
+  };
+  auto load_block = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int id = tid + i * NTHR;
+      kst[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (id < KCH) {
+        const int key = id / (D / 8), seg = id % (D / 8);
+        const int j = blk + key;
+        if (j < kend) kst[i] = *reinterpret_cast<const uint4*>(key_src(j, kc, kn) + seg * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int id = tid + i * NTHR;
+      vst[i][0] = vst[i][1] = make_uint4(0u, 0u, 0u, 0u);
+      if (id < VUN) {
+        const int kp = id % (BK / 2), ds = id / (BK / 2);
+        const int j = blk + 2 * kp;
+        if (j < kend) vst[i][0] = *reinterpret_cast<const uint4*>(key_src(j, vc, vn) + ds * 8);
+        if (j + 1 < kend) vst[i][1] = *reinterpret_cast<const uint4*>(key_src(j + 1, vc, vn) + ds * 8);
+      }
+    }
+  };
+  auto store_block = [&](int buf) {
+    __bf16* ks = smem + buf * STAGE;
+    __bf16* vs = ks + K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int id = tid + i * NTHR;
+      if (id < KCH) {
+        const int key = id / (D / 8), seg = id % (D / 8);
+        *reinterpret_cast<uint4*>(ks + key * KS + seg * 8) = kst[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int id = tid + i * NTHR;
+      if (id < VUN) {
+        const int kp = id % (BK / 2), ds = id / (BK / 2);
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(&vst[i][0]);
+        const uint32_t* bb = reinterpret_cast<const uint32_t*>(&vst[i][1]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t lo = (e & 1) ? (a[e >> 1] >> 16) : (a[e >> 1] & 0xFFFFu);
+          const uint32_t hi = (e & 1) ? (bb[e >> 1] & 0xFFFF0000u) : (bb[e >> 1] << 16);
+          *reinterpret_cast<uint32_t*>(vs + (ds * 8 + e) * VS + 2 * kp) = lo | hi;
+        }
+      }
+    }
+  };
+
+  const int nblk = (kend - kbeg + BK - 1) / BK;
+  load_block(kbeg);
+  store_block(0);
+  __syncthreads();
+
+  for (int it = 0; it < nblk; ++it) {
+    const int blk = kbeg + it * BK;
+    const int buf = it & 1;
+    if (it + 1 < nblk) load_block(blk + BK);
+    const __bf16* ks = smem + buf * STAGE;
+    const __bf16* vs = ks + K_ELEMS;
+
+    // ---- scores S^T (2 sub-tiles of 16 keys)
+    f32x4 s[NT][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * kt + c) * KS + 32 * kk + 8 * g);
+#pragma unroll
+        for (int qt = 0; qt < NT; ++qt)
+          s[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a, qreg[qt][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[qt][kt], 0, 0, 0);
+      }
+    }
+
+    // ---- mask: keys past the range end, and tree keys that are not ancestors.
+    // Visibility of the block's 32 keys for this lane's row, as one word:
+    // bit o <=> key blk + o is a prefix key, or a tree key whose node is an
+    // ancestor-or-self of the row's node, and lies before kend.
+    if (blk + BK > Lb || blk + BK > kend) {
+      const int n0 = blk - Lb;                      // node index of the block's first key
+      const uint32_t range_bits = (kend - blk >= 32) ? 0xFFFFFFFFu : ((1u << (kend - blk)) - 1u);
+      const uint32_t prefix_bits = (n0 >= 0) ? 0u : (-n0 >= 32 ? 0xFFFFFFFFu : ((1u << -n0) - 1u));
+#pragma unroll
+      for (int qt = 0; qt < NT; ++qt) {
+        const int t = rrow[qt] / G;
+        uint32_t tree_bits = 0u;
+        if (rvalid[qt] && n0 + BK > 0) {
+          const uint64_t* arow = anc_s + t * W;
+          // bits [n0, n0 + 32) of the row (bits below 0 are empty)
+          const int lo = n0 < 0 ? 0 : n0;
+          const int w = lo >> 6, sh = lo & 63;
+          uint64_t bits = arow[w] >> sh;
+          if (sh > 32 && w + 1 < W) bits |= arow[w + 1] << (64 - sh);
+          tree_bits = (uint32_t)bits;
+          if (n0 < 0) tree_bits <<= -n0;            // node 0 sits at key offset -n0
+        }
+        const uint32_t vm = (prefix_bits | tree_bits) & range_bits;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int o = 16 * kt + 4 * g + i;
+            s[qt][kt][i] = ((vm >> o) & 1u) ? s[qt][kt][i] : -INFINITY;
+          }
+      }
+    }
+
+    // ---- online softmax (exp2, scale folded), P packed to bf16 for the PV MFMA
+    bf16x8 pk[NT];
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+      float mx = fmaxf(fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3])),
+                       fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3])));
+      mx = wave_max16_32(mx) * p.scale_log2;
+      const bool need = mx > m_run[qt] + 8.0f;
+      if (__any(need)) {
+        const float mnew = need ? mx : m_run[qt];
+        const float alpha = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - mnew);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
+        l_part[qt] *= alpha;
+        m_run[qt] = mnew;
+      }
+      const float mu = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+      float pv[8];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[kt * 4 + i] = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][i], p.scale_log2, -mu));
+      l_part[qt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
+      pk[qt] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const __bf16* vrow = vs + (16 * dt + c) * VS + 4 * g;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int qt = 0; qt < NT; ++qt)
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[qt], acc[qt][dt], 0, 0, 0);
+    }
+
+    if (it + 1 < nblk) store_block(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int qt = 0; qt < NT; ++qt) {
+    const float l = wave_sum16_32(l_part[qt]);
+    const int r = rrow[qt];
+    if (r >= p.T_max * G) continue;
+    const int t = r / G, h = kvh * G + r % G;
+    const size_t orow = ((size_t)b * p.T_max + t) * p.Hq + h;
+    if (p.lsplit == 1) {
+      __bf16* o = reinterpret_cast<__bf16*>(p.out) + orow * D;
+      const float inv = (rvalid[qt] && l > 0.f) ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 v = acc[qt][dt] * inv;
+        *reinterpret_cast<uint2*>(o + dt * 16 + 4 * g) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    } else if (rvalid[qt]) {
+      float* po = p.part_o + (orow * p.lsplit + ls_i) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
+            make_float4(acc[qt][dt][0], acc[qt][dt][1], acc[qt][dt][2], acc[qt][dt][3]);
+      if (g == 0) {
+        float* pm = p.part_ml + (orow * p.lsplit + ls_i) * 2;
+        pm[0] = m_run[qt];
+        pm[1] = l;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// fp32 kernel (VALU): one wave per (sequence, tree position, query head) row,
+// keys in blocks of 64 (one per lane), lane d owns output dims d and d + 64.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void k_attn_f32(AttnParams p) {
+  __shared__ float qs[D];
+  __shared__ float ps[64];
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;                  // ((b * T_max + t) * Hq + h)
+  const int ls_i = blockIdx.y;
+  const int h = row % p.Hq;
+  const int t = (row / p.Hq) % p.T_max;
+  const int b = row / (p.Hq * p.T_max);
+  const int kvh = h / p.G;
+  const int Tb = p.num_nodes[b];
+  const int Lb = p.prefix_len[b];
+  const bool valid = p.status[b] == SV_TREE_OK && t < Tb && Tb <= p.T_max && Lb >= 0 && Lb <= p.L_max;
+  const int kbeg = ls_i * p.chunk;
+  const int kend = min(kbeg + p.chunk, Lb + Tb);
+  constexpr int DPL = D / 64 > 0 ? D / 64 : 1;  // output dims per lane
+
+  float o[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (valid && kbeg < kend) {
+    const float* qp = reinterpret_cast<const float*>(p.q) + (size_t)row * D;
+    for (int d = lane; d < D; d += 64) qs[d] = qp[d];
+    __syncthreads();
+    const float* kc = reinterpret_cast<const float*>(p.k_cache) + ((size_t)b * p.Hkv + kvh) * p.L_max * D;
+    const float* vc = reinterpret_cast<const float*>(p.v_cache) + ((size_t)b * p.Hkv + kvh) * p.L_max * D;
+    const float* kn = reinterpret_cast<const float*>(p.k_new) + ((size_t)b * p.T_max * p.Hkv + kvh) * D;
+    const float* vn = reinterpret_cast<const float*>(p.v_new) + ((size_t)b * p.T_max * p.Hkv + kvh) * D;
+    const size_t ns = (size_t)p.Hkv * D;
+    const uint64_t* arow = p.anc + ((size_t)b * p.T_max + t) * p.W;
+    for (int blk = kbeg; blk < kend; blk += 64) {
+      const int j = blk + lane;
+      float sc = -INFINITY;
+      bool vis = j < kend;
+      if (vis && j >= Lb) {
+        const int n = j - Lb;
+        vis = (arow[n >> 6] >> (n & 63)) & 1ull;
+      }
+      if (vis) {
+        const float* kr = j < Lb ? kc + (size_t)j * D : kn + (size_t)(j - Lb) * ns;
+        float dot = 0.f;
+        for (int d = 0; d < D; ++d) dot = fmaf(qs[d], kr[d], dot);
+        sc = dot * p.scale_log2;
+      }
+      float mx = sc;
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mnew = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - mnew);
+      const float pe = sc == -INFINITY ? 0.f : exp2f(sc - mnew);
+      float ssum = pe;
+      for (int off = 32; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off);
+      l_run = l_run * alpha + ssum;
+      m_run = mnew;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[k] *= alpha;
+      ps[lane] = pe;
+      __syncthreads();
+      const int nk = min(64, kend - blk);
+      for (int kk = 0; kk < nk; ++kk) {
+        const float w = ps[kk];
+        if (w == 0.f) continue;
+        const int jj = blk + kk;
+        const float* vr = jj < Lb ? vc + (size_t)jj * D : vn + (size_t)(jj - Lb) * ns;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+          if (lane + 64 * k < D) o[k] = fmaf(w, vr[lane + 64 * k], o[k]);
+      }
+      __syncthreads();
+    }
+  }
+  if (p.lsplit == 1) {
+    float* out = reinterpret_cast<float*>(p.out) + (size_t)row * D;
+    const float inv = (valid && l_run > 0.f) ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      if (lane + 64 * k < D) out[lane + 64 * k] = o[k] * inv;
+  } else if (valid) {
+    float* po = p.part_o + ((size_t)row * p.lsplit + ls_i) * D;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      if (lane + 64 * k < D) po[lane + 64 * k] = o[k];
+    if (lane == 0) {
+      p.part_ml[((size_t)row * p.lsplit + ls_i) * 2] = m_run;
+      p.part_ml[((size_t)row * p.lsplit + ls_i) * 2 + 1] = l_run;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Merge of key-range partials: m = max m_s, O = sum 2^(m_s - m) O_s / sum
+// 2^(m_s - m) l_s.  One wave per output row; invalid rows are zeroed.
+// ----------------------------------------------------------------------------
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
+  const int t = (row / p.Hq) % p.T_max;
+  const int b = row / (p.Hq * p.T_max);
+  const int Tb = p.num_nodes[b];
+  const int Lb = p.prefix_len[b];
+  const bool valid = p.status[b] == SV_TREE_OK && t < Tb && Tb <= p.T_max && Lb >= 0 && Lb <= p.L_max;
+  constexpr int DPL = D / 64;
+  float o[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+  if (valid) {
+    const float* pm = p.part_ml + (size_t)row * p.lsplit * 2;
+    float m = -INFINITY;
+    for (int s = 0; s < p.lsplit; ++s) m = fmaxf(m, pm[2 * s]);
+    float l = 0.f;
+    for (int s = 0; s < p.lsplit; ++s) {
+      const float ms = pm[2 * s];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - m);
+      l += w * pm[2 * s + 1];
+      const float* po = p.part_o + ((size_t)row * p.lsplit + s) * D;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[k] = fmaf(w, po[lane + 64 * k], o[k]);
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] *= inv;
+  }
+  if (BF16) {
+    __bf16* out = reinterpret_cast<__bf16*>(p.out) + (size_t)row * D;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) out[lane + 64 * k] = (__bf16)o[k];
+  } else {
+    float* out = reinterpret_cast<float*>(p.out) + (size_t)row * D;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) out[lane + 64 * k] = o[k];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// host side: launch planning
+// ----------------------------------------------------------------------------
+namespace {
+struct Variant {
+  int D, nt, nw;
+  float row_cost;  // relative cost of one padded row
+};
+// Instantiated MFMA shapes (head dim, 16-row tiles per wave, waves per group);
+// all of them fit two waves per SIMD.
+const Variant kVariants[] = {
+    {128, 3, 4, 1.0f}, {128, 2, 4, 1.0f}, {128, 2, 1, 1.0f}, {128, 1, 1, 1.0f},
+    {64, 4, 4, 1.0f},  {64, 3, 4, 1.0f},  {64, 2, 1, 1.0f},  {64, 1, 1, 1.0f},
+};
+// One more pass over the keys of a (sequence, KV head), in padded-row units.
+constexpr float kRereadRows = 160.f;
+
+size_t smem_bytes(int D, int T_max) {
+  const int W = (T_max + 63) / 64;
+  const size_t stage = (size_t)BK * (D + 8) + (size_t)D * (BK + 4);
+  return 2 * stage * sizeof(uint16_t) + (size_t)T_max * W * sizeof(uint64_t);
+}
+}  // namespace
+
+bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* pl) {
+  const DeviceInfo& di = device_info();
+  const int G = a->Hq / a->Hkv;
+  const long M = (long)t->T_max * G;  // padded query rows per (sequence, KV head)
+  const long units = (long)t->B * a->Hkv;
+  const long keys = (long)a->L_max + t->T_max;
+  *pl = AttnPlan{};
+  if (a->dtype == SV_F32) {
+    pl->kernel = 1;
+    const long rows = (long)t->B * t->T_max * a->Hq;
+    long ls = 1;
+    while (rows * ls < 4L * di.num_cu && keys / (ls * 2) >= 256) ls *= 2;
+    pl->lsplit = (int)ls;
+  } else {
+    pl->kernel = 0;
+    // choose the variant with the least padded row work; more rows per
+    // workgroup (fewer re-reads of the same keys) breaks ties
+    float best_cost = -1.f;
+    for (const Variant& v : kVariants) {
+      if (v.D != a->D) continue;
+      const long rpw = (long)v.nt * v.nw * 16;
+      const long ms = (M + rpw - 1) / rpw;
+      const float cost = (float)(ms * rpw) * v.row_cost + kRereadRows * (float)ms;
+      if (best_cost < 0.f || cost < best_cost) {
+        best_cost = cost;
+        pl->nt = v.nt;
+        pl->nwave = v.nw;
+        pl->rows_per_wg = (int)rpw;
+        pl->msplit = (int)ms;
+      }
+    }
+    if (best_cost < 0.f) return false;
+    // tuning override: SV_ATTN_VARIANT="nt,nw" picks an instantiated shape
+    if (const char* ov = getenv("SV_ATTN_VARIANT")) {
+      int nt = 0, nw = 0;
+      if (sscanf(ov, "%d,%d", &nt, &nw) == 2) {
+        for (const Variant& v : kVariants) {
+          if (v.D == a->D && v.nt == nt && v.nw == nw) {
+            const long rpw = (long)nt * nw * 16;
+            pl->nt = nt;
+            pl->nwave = nw;
+            pl->rows_per_wg = (int)rpw;
+            pl->msplit = (int)((M + rpw - 1) / rpw);
+          }
+        }
+      }
+    }
+    long groups = units * pl->msplit;
+    long ls = 1;
+    while (groups * ls < 2L * di.num_cu && keys / (ls * 2) >= 8L * BK) ls *= 2;
+    pl->lsplit = (int)ls;
+  }
+  // tuning override: SV_ATTN_LSPLIT=n forces n key ranges per row
+  if (const char* ov = getenv("SV_ATTN_LSPLIT")) {
+    const int n = atoi(ov);
+    if (n >= 1 && n <= 64) pl->lsplit = n;
+  }
+  const long per = (keys + pl->lsplit - 1) / pl->lsplit;
+  pl->chunk = (int)((per + 63) / 64 * 64);
+  pl->ws_bytes = 0;
+  if (pl->lsplit > 1) {
+    const size_t rows = (size_t)t->B * t->T_max * a->Hq * pl->lsplit;
+    pl->ws_bytes = align_up(rows * a->D * sizeof(float), kWsAlign) +
+                   align_up(rows * 2 * sizeof(float), kWsAlign);
+  }
+  return true;
+}
+
+template <int D, int NT, int NW>
+static hipError_t launch_mfma(const AttnParams& prm, int grid, size_t smem, hipStream_t s) {
+  auto k = k_attn_bf16<D, NT, NW>;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev < 64 && !attr_set[dev]) {
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), smem, s, prm);
+  return hipGetLastError();
+}
+
+sv_status launch_attention(const sv_tree* t, const uint64_t* anc, const int32_t* tree_status,
+                           const sv_attn_args* a, const AttnPlan& pl, void* ws, hipStream_t s) {
+  if (t->B == 0) return SV_OK;
+  AttnParams prm{};
+  prm.q = a->q;
+  prm.k_new = a->k_new;
+  prm.v_new = a->v_new;
+  prm.k_cache = a->k_cache;
+  prm.v_cache = a->v_cache;
+  prm.prefix_len = a->prefix_len;
+  prm.num_nodes = t->num_nodes;
+  prm.status = tree_status;
+  prm.anc = anc;
+  prm.out = a->out;
+  prm.B = t->B;
+  prm.T_max = t->T_max;
+  prm.Hq = a->Hq;
+  prm.Hkv = a->Hkv;
+  prm.G = a->Hq / a->Hkv;
+  prm.L_max = a->L_max;
+  prm.W = (t->T_max + 63) / 64;
+  prm.rows_per_wg = pl.rows_per_wg;
+  prm.msplit = pl.msplit;
+  prm.lsplit = pl.lsplit;
+  prm.chunk = pl.chunk;
+  const double scale = a->scale > 0.f ? (double)a->scale : 1.0 / sqrt((double)a->D);
+  prm.scale_log2 = (float)(scale * 1.4426950408889634);
+  if (pl.lsplit > 1) {
+    const size_t rows = (size_t)t->B * t->T_max * a->Hq * pl.lsplit;
+    prm.part_o = reinterpret_cast<float*>(ws);
+    prm.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * a->D * sizeof(float), kWsAlign));
+  }
+  hipError_t e = hipSuccess;
+  if (pl.kernel == 1) {
+    const int rows = t->B * t->T_max * a->Hq;
+    dim3 grid(rows, pl.lsplit);
+    if (a->D == 64) hipLaunchKernelGGL(k_attn_f32<64>, grid, dim3(64), 0, s, prm);
+    else hipLaunchKernelGGL(k_attn_f32<128>, grid, dim3(64), 0, s, prm);
+    e = hipGetLastError();
+  } else {
+    const int grid = (int)((long)t->B * a->Hkv * pl.msplit * pl.lsplit);
+    prm.remap = (grid % 8 == 0) ? 1 : 0;
+    const size_t smem = smem_bytes(a->D, t->T_max);
+    const int key = a->D * 100 + pl.nt * 10 + pl.nwave;
+    switch (key) {
+      case 12834: e = launch_mfma<128, 3, 4>(prm, grid, smem, s); break;
+      case 12824: e = launch_mfma<128, 2, 4>(prm, grid, smem, s); break;
+      case 12821: e = launch_mfma<128, 2, 1>(prm, grid, smem, s); break;
+      case 12811: e = launch_mfma<128, 1, 1>(prm, grid, smem, s); break;
+      case 6444: e = launch_mfma<64, 4, 4>(prm, grid, smem, s); break;
+      case 6434: e = launch_mfma<64, 3, 4>(prm, grid, smem, s); break;
+      case 6421: e = launch_mfma<64, 2, 1>(prm, grid, smem, s); break;
+      case 6411: e = launch_mfma<64, 1, 1>(prm, grid, smem, s); break;
+      default: set_error("no attention variant D=%d nt=%d nw=%d", a->D, pl.nt, pl.nwave); return SV_E_UNSUPPORTED;
+    }
+  }
+  if (e != hipSuccess) {
+    set_error("attention launch: %s", hipGetErrorString(e));
+    return SV_E_HIP;
+  }
+  if (pl.lsplit > 1) {
+    const int rows = t->B * t->T_max * a->Hq;
+    if (a->dtype == SV_BF16) {
+      if (a->D == 64) hipLaunchKernelGGL((k_attn_combine<true, 64>), dim3(rows), dim3(64), 0, s, prm);
+      else hipLaunchKernelGGL((k_attn_combine<true, 128>), dim3(rows), dim3(64), 0, s, prm);
+    } else {
+      if (a->D == 64) hipLaunchKernelGGL((k_attn_combine<false, 64>), dim3(rows), dim3(64), 0, s, prm);
+      else hipLaunchKernelGGL((k_attn_combine<false, 128>), dim3(rows), dim3(64), 0, s, prm);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      set_error("attention combine launch: %s", hipGetErrorString(e));
+      return SV_E_HIP;
+    }
+  }
+  return SV_OK;
+}
+
+}  // namespace sv

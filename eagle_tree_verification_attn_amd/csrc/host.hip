@@ -1,0 +1,215 @@
+// C ABI of the verification library: argument validation, workspace sizing,
+// launch sequencing.  Every entry point only enqueues work on the caller's
+// stream; nothing here allocates device memory or synchronises.
+#include "sv_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace sv {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+void clear_error() { g_err[0] = 0; }
+
+const DeviceInfo& device_info() {
+  static DeviceInfo infos[64];
+  static bool have[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!have[dev]) {
+    DeviceInfo d{dev, 256, 8};
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+      d.num_cu = cu;
+    infos[dev] = d;
+    have[dev] = true;
+  }
+  return infos[dev];
+}
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+sv_status check_tree(const sv_tree* t, bool need_tokens) {
+  if (!t) { set_error("tree is NULL"); return SV_E_NULL; }
+  if (t->B < 0) { set_error("B = %d < 0", t->B); return SV_E_SHAPE; }
+  if (t->T_max < 1) { set_error("T_max = %d < 1", t->T_max); return SV_E_SHAPE; }
+  if (t->T_max > kMaxT) { set_error("T_max = %d > %d", t->T_max, kMaxT); return SV_E_UNSUPPORTED; }
+  if (t->B > 0) {
+    if (!t->parent || !t->num_nodes) { set_error("tree parent/num_nodes is NULL"); return SV_E_NULL; }
+    if (need_tokens && !t->tokens) { set_error("tree tokens is NULL"); return SV_E_NULL; }
+  }
+  return SV_OK;
+}
+
+sv_status check_attn(const sv_tree* t, const sv_attn_args* a) {
+  if (!a) { set_error("attention args are NULL"); return SV_E_NULL; }
+  if (a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0) {
+    set_error("heads Hq=%d Hkv=%d (need Hq %% Hkv == 0)", a->Hq, a->Hkv);
+    return SV_E_SHAPE;
+  }
+  if (a->D < 1 || a->L_max < 0) { set_error("D=%d L_max=%d", a->D, a->L_max); return SV_E_SHAPE; }
+  if (a->D != 64 && a->D != 128) { set_error("head dim %d (supported: 64, 128)", a->D); return SV_E_UNSUPPORTED; }
+  if (a->dtype != SV_F32 && a->dtype != SV_BF16) { set_error("attention dtype %d", a->dtype); return SV_E_DTYPE; }
+  if ((long)t->B * t->T_max * a->Hq > 0x7FFFFFFFL) { set_error("B*T_max*Hq too large"); return SV_E_UNSUPPORTED; }
+  if (t->B > 0) {
+    if (!a->q || !a->k_new || !a->v_new || !a->out || !a->prefix_len) {
+      set_error("attention q/k_new/v_new/out/prefix_len is NULL");
+      return SV_E_NULL;
+    }
+    if (a->L_max > 0 && (!a->k_cache || !a->v_cache)) { set_error("k_cache/v_cache is NULL"); return SV_E_NULL; }
+    const void* ptrs[] = {a->q, a->k_new, a->v_new, a->out, a->k_cache, a->v_cache};
+    for (const void* p : ptrs)
+      if (p && !aligned(p, 16)) { set_error("attention tensors must be 16-byte aligned"); return SV_E_UNSUPPORTED; }
+  }
+  return SV_OK;
+}
+
+sv_status check_accept(const sv_tree* t, const sv_accept_args* a) {
+  if (!a) { set_error("accept args are NULL"); return SV_E_NULL; }
+  if (a->V < 1) { set_error("V = %d < 1", a->V); return SV_E_SHAPE; }
+  if (a->V > 64 * 256 * 64) { set_error("V = %d > %d", a->V, 64 * 256 * 64); return SV_E_UNSUPPORTED; }
+  if (a->logit_dtype != SV_F32 && a->logit_dtype != SV_BF16) { set_error("logit dtype %d", a->logit_dtype); return SV_E_DTYPE; }
+  if (a->sibling_mode != SV_SIB_WITHOUT_REPLACEMENT && a->sibling_mode != SV_SIB_IID) {
+    set_error("sibling_mode %d", a->sibling_mode);
+    return SV_E_SHAPE;
+  }
+  if ((long)t->B * t->T_max > 0x7FFFFFFFL / 64) { set_error("B*T_max too large"); return SV_E_UNSUPPORTED; }
+  if (t->B > 0) {
+    if (!a->target_logits || !a->temperature || !a->u_accept || !a->u_sample || !a->out_tokens ||
+        !a->out_nodes || !a->out_count) {
+      set_error("accept logits/temperature/uniforms/outputs is NULL");
+      return SV_E_NULL;
+    }
+  }
+  return SV_OK;
+}
+
+sv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SV_OK;
+  if (!ws) { set_error("workspace is NULL (need %zu bytes)", need); return SV_E_WORKSPACE; }
+  if (ws_bytes < need) { set_error("workspace %zu bytes < %zu needed", ws_bytes, need); return SV_E_WORKSPACE; }
+  if (!aligned(ws, kWsAlign)) { set_error("workspace not %zu-byte aligned", kWsAlign); return SV_E_WORKSPACE; }
+  return SV_OK;
+}
+
+}  // namespace
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+sv_status sv_tree_mask_build(const sv_tree* tree, uint64_t* anc, int32_t* depth, int32_t* tree_status,
+                             void* stream) {
+  clear_error();
+  sv_status st = check_tree(tree, false);
+  if (st) return st;
+  if (tree->B > 0 && (!anc || !depth || !tree_status)) { set_error("anc/depth/tree_status is NULL"); return SV_E_NULL; }
+  return launch_mask(tree, anc, depth, tree_status, (hipStream_t)stream);
+}
+
+sv_status sv_tree_attn(const sv_tree* tree, const uint64_t* anc, const int32_t* tree_status,
+                       const sv_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  sv_status st = check_tree(tree, false);
+  if (st) return st;
+  if ((st = check_attn(tree, a))) return st;
+  if (tree->B > 0 && (!anc || !tree_status)) { set_error("anc/tree_status is NULL"); return SV_E_NULL; }
+  AttnPlan pl;
+  if (!plan_attention(tree, a, &pl)) { set_error("no attention plan"); return SV_E_UNSUPPORTED; }
+  if ((st = check_ws(ws, ws_bytes, pl.ws_bytes))) return st;
+  return launch_attention(tree, anc, tree_status, a, pl, ws, (hipStream_t)stream);
+}
+
+sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_accept_args* a, void* ws,
+                         size_t ws_bytes, void* stream) {
+  clear_error();
+  sv_status st = check_tree(tree, true);
+  if (st) return st;
+  if ((st = check_accept(tree, a))) return st;
+  if (tree->B > 0 && !tree_status) { set_error("tree_status is NULL"); return SV_E_NULL; }
+  AcceptPlan pl;
+  if (!plan_accept(tree, a, &pl)) { set_error("no accept plan"); return SV_E_UNSUPPORTED; }
+  if ((st = check_ws(ws, ws_bytes, pl.ws_bytes))) return st;
+  return launch_accept(tree, tree_status, a, pl, ws, (hipStream_t)stream);
+}
+
+sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
+                         uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws, size_t ws_bytes,
+                         void* stream) {
+  clear_error();
+  sv_status st = check_tree(tree, true);
+  if (st) return st;
+  if ((st = check_attn(tree, attn))) return st;
+  if ((st = check_accept(tree, acc))) return st;
+  if (tree->B > 0 && (!anc || !depth || !tree_status)) { set_error("anc/depth/tree_status is NULL"); return SV_E_NULL; }
+  AttnPlan ap;
+  AcceptPlan cp;
+  if (!plan_attention(tree, attn, &ap)) { set_error("no attention plan"); return SV_E_UNSUPPORTED; }
+  if (!plan_accept(tree, acc, &cp)) { set_error("no accept plan"); return SV_E_UNSUPPORTED; }
+  const size_t need = ap.ws_bytes > cp.ws_bytes ? ap.ws_bytes : cp.ws_bytes;
+  if ((st = check_ws(ws, ws_bytes, need))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = launch_mask(tree, anc, depth, tree_status, s))) return st;
+  if ((st = launch_attention(tree, anc, tree_status, attn, ap, ws, s))) return st;
+  return launch_accept(tree, tree_status, acc, cp, ws, s);
+}
+
+size_t sv_workspace_bytes(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc) {
+  clear_error();
+  // sizing reads only the scalar fields: pointers may be NULL here
+  if (!tree) { set_error("tree is NULL"); return 0; }
+  if (tree->B < 0 || tree->T_max < 1 || tree->T_max > kMaxT) { set_error("B=%d T_max=%d", tree->B, tree->T_max); return 0; }
+  size_t need = 0;
+  if (attn) {
+    if (attn->Hq < 1 || attn->Hkv < 1 || attn->Hq % attn->Hkv || (attn->D != 64 && attn->D != 128) ||
+        attn->L_max < 0 || (attn->dtype != SV_F32 && attn->dtype != SV_BF16)) {
+      set_error("attention sizes Hq=%d Hkv=%d D=%d L_max=%d dtype=%d", attn->Hq, attn->Hkv, attn->D, attn->L_max, attn->dtype);
+      return 0;
+    }
+    AttnPlan pl;
+    if (!plan_attention(tree, attn, &pl)) return 0;
+    need = pl.ws_bytes;
+  }
+  if (acc) {
+    if (acc->V < 1) { set_error("V = %d < 1", acc->V); return 0; }
+    AcceptPlan pl;
+    if (!plan_accept(tree, acc, &pl)) { set_error("V = %d unsupported", acc->V); return 0; }
+    if (pl.ws_bytes > need) need = pl.ws_bytes;
+  }
+  return need;
+}
+
+const char* sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_E_NULL: return "null pointer argument";
+    case SV_E_SHAPE: return "invalid size or shape";
+    case SV_E_DTYPE: return "unknown dtype";
+    case SV_E_WORKSPACE: return "workspace missing, too small or misaligned";
+    case SV_E_HIP: return "HIP runtime or launch failure";
+    case SV_E_UNSUPPORTED: return "unsupported configuration";
+    case SV_TREE_E_ROOT: return "tree: root has a parent";
+    case SV_TREE_E_PARENT: return "tree: parent index not in [0, i)";
+    case SV_TREE_E_COUNT: return "tree: node count outside [1, T_max]";
+    case SV_TREE_E_TOKEN: return "tree: token outside [0, V)";
+    case SV_TREE_E_NONFINITE: return "tree: non-finite target logit";
+    case SV_TREE_E_NOQ: return "tree: stochastic sequence without draft probabilities";
+    case SV_TREE_E_SYNC: return "tree: cross-workgroup wait timed out";
+    default: return "unknown status";
+  }
+}
+
+const char* sv_last_error(void) { return g_err; }
+
+}  // extern "C"

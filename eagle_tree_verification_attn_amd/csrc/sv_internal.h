@@ -1,0 +1,64 @@
+// Internal declarations shared by the HIP sources of the verification library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "sv.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxT = 256;          // largest T_max (one mask row per thread)
+constexpr size_t kWsAlign = 256;    // workspace sub-buffer alignment
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Thread-local detail string behind sv_last_error().
+void set_error(const char* fmt, ...);
+void clear_error();
+
+// Per-device facts used to size launches (cached on first use per device).
+struct DeviceInfo {
+  int device;
+  int num_cu;
+  int num_xcd;
+};
+const DeviceInfo& device_info();
+
+// ---------------------------------------------------------------- attention
+struct AttnPlan {
+  int kernel;       // 0 = bf16 MFMA, 1 = fp32 VALU
+  int nt;           // 16-query tiles per wave (MFMA kernel)
+  int nwave;        // waves per workgroup (MFMA kernel)
+  int rows_per_wg;  // query rows (node, head-in-group pairs) per workgroup
+  int msplit;       // workgroups along the query rows of one (sequence, KV head)
+  int lsplit;       // workgroups along the key axis
+  int chunk;        // keys per L split (multiple of the key block)
+  size_t ws_bytes;  // partial results when lsplit > 1
+};
+bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* p);
+sv_status launch_attention(const sv_tree* t, const uint64_t* anc, const int32_t* tree_status,
+                           const sv_attn_args* a, const AttnPlan& p, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- accept
+struct AcceptPlan {
+  int nchunk;       // vocabulary chunks per row (= workgroups per sequence in the walk)
+  int chunk;        // tokens per chunk (multiple of 8)
+  int ngroups;      // sequence groups resident at once in the walk
+  int stats_threads;
+  size_t off_stats, off_sync, off_part;
+  size_t ws_bytes;
+};
+bool plan_accept(const sv_tree* t, const sv_accept_args* a, AcceptPlan* p);
+sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_args* a,
+                        const AcceptPlan& p, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- mask
+sv_status launch_mask(const sv_tree* t, uint64_t* anc, int32_t* depth, int32_t* tree_status,
+                      hipStream_t s);
+
+}  // namespace sv

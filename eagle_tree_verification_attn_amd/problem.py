@@ -1,0 +1,109 @@
+"""Device-side buffers for one verification problem (argument marshalling).
+
+``DeviceProblem`` uploads host arrays (NumPy; bf16 data as uint16 bit
+patterns) to torch tensors on the GPU, allocates the outputs and the workspace,
+and builds the C-ABI structs.  Its methods call the library's entry points on
+the current torch stream.  Nothing here computes any part of the verification.
+"""
+import numpy as np
+
+from . import (SV_SIB_IID, SV_SIB_WITHOUT_REPLACEMENT, make_accept_args, make_attn_args, make_tree,
+               sv_spec_accept, sv_tree_attn, sv_tree_mask_build, sv_verify_step, sv_workspace_bytes)
+
+
+def to_device(arr, dtype, device):
+    """NumPy -> torch on ``device``; dtype 'bf16' reads uint16 bit patterns."""
+    import torch
+    a = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def bf16_bits(t):
+    """torch bfloat16 tensor -> NumPy uint16 bit patterns (host)."""
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DeviceProblem:
+    """Inputs, outputs and workspace of one batch on one GPU.
+
+    ``src`` is any object with the attributes of a problem instance: B, T_max,
+    parent, num_nodes, tokens, and for attention q, k_new, v_new, k_cache,
+    v_cache, prefix_len, dtype; for acceptance target_logits, logit_dtype,
+    q_probs, temperature, u_accept, u_sample, sibling_mode.
+    """
+
+    def __init__(self, src, device="cuda", with_attn=True, with_accept=True, scale=0.0):
+        import torch
+        self.device = device
+        B, T = int(src.B), int(src.T_max)
+        self.B, self.T_max = B, T
+        i32 = lambda a: to_device(np.asarray(a, dtype=np.int32), "i32", device)
+        self.parent = i32(src.parent)
+        self.num_nodes = i32(src.num_nodes)
+        self.tokens = i32(src.tokens)
+        self.tree = make_tree(self.parent, self.num_nodes, self.tokens)
+        W = (T + 63) // 64
+        self.anc = torch.zeros((B, T, W), dtype=torch.int64, device=device)
+        self.depth = torch.zeros((B, T), dtype=torch.int32, device=device)
+        self.status = torch.zeros((B,), dtype=torch.int32, device=device)
+        self.attn = None
+        self.acc = None
+        if with_attn and getattr(src, "q", None) is not None:
+            dt = src.dtype
+            self.q = to_device(src.q, dt, device)
+            self.k_new = to_device(src.k_new, dt, device)
+            self.v_new = to_device(src.v_new, dt, device)
+            self.k_cache = to_device(src.k_cache, dt, device)
+            self.v_cache = to_device(src.v_cache, dt, device)
+            self.prefix_len = i32(src.prefix_len)
+            self.out = torch.empty_like(self.q)
+            self.attn = make_attn_args(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache,
+                                       self.prefix_len, self.out, scale)
+        if with_accept and getattr(src, "target_logits", None) is not None:
+            self.logits = to_device(src.target_logits, src.logit_dtype, device)
+            self.q_probs = None if src.q_probs is None else to_device(src.q_probs, "f32", device)
+            self.temperature = to_device(np.asarray(src.temperature, dtype=np.float32), "f32", device)
+            self.u_accept = to_device(np.asarray(src.u_accept, dtype=np.float32), "f32", device)
+            self.u_sample = to_device(np.asarray(src.u_sample, dtype=np.float32), "f32", device)
+            self.out_tokens = torch.full((B, T), -7, dtype=torch.int32, device=device)
+            self.out_nodes = torch.full((B, T), -7, dtype=torch.int32, device=device)
+            self.out_count = torch.full((B,), -7, dtype=torch.int32, device=device)
+            self.out_passes = torch.full((B,), -7, dtype=torch.int32, device=device)
+            mode = SV_SIB_IID if getattr(src, "sibling_mode", "wor") == "iid" else SV_SIB_WITHOUT_REPLACEMENT
+            self.acc = make_accept_args(self.logits, self.q_probs, self.temperature, self.u_accept,
+                                        self.u_sample, self.out_tokens, self.out_nodes, self.out_count,
+                                        self.out_passes, mode)
+        nbytes = sv_workspace_bytes(self.tree, self.attn, self.acc)
+        self.ws = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+
+    # ---- entry points on this problem
+    def mask_build(self, stream=None):
+        return sv_tree_mask_build(self.tree, self.anc, self.depth, self.status, stream)
+
+    def tree_attn(self, stream=None):
+        return sv_tree_attn(self.tree, self.anc, self.status, self.attn, self.ws, stream)
+
+    def spec_accept(self, stream=None):
+        return sv_spec_accept(self.tree, self.status, self.acc, self.ws, stream)
+
+    def verify_step(self, stream=None):
+        return sv_verify_step(self.tree, self.attn, self.acc, self.anc, self.depth, self.status,
+                              self.ws, stream)
+
+    # ---- results on the host
+    def mask_results(self):
+        return (self.anc.cpu().numpy().view(np.uint64), self.depth.cpu().numpy(),
+                self.status.cpu().numpy())
+
+    def attn_result(self):
+        """Attention output as float64 on the host."""
+        import torch
+        return self.out.to(torch.float64).cpu().numpy()
+
+    def accept_results(self):
+        return dict(out_nodes=self.out_nodes.cpu().numpy(), out_tokens=self.out_tokens.cpu().numpy(),
+                    out_count=self.out_count.cpu().numpy(), out_passes=self.out_passes.cpu().numpy(),
+                    status=self.status.cpu().numpy())

@@ -1,0 +1,196 @@
+/*
+ * sv.h -- draft-tree verification on AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * One verification step of EAGLE-style speculative decoding, as described on
+ *   [EAGLE article]  the course.zhidx.com mirror of the Zhihu article on
+ *                    EAGLE / EAGLE-2 / EAGLE-3 / DFlash: section 1.3
+ *                    "Verification" (one target forward scores the whole draft
+ *                    tree with tree attention; speculative sampling is applied
+ *                    recursively at every node, with k sibling candidates tried
+ *                    in turn, Figure 1-6) and section 2.3 "Flatten + Attention
+ *                    mask" (each token sees only its ancestors, Figure 2-7);
+ *   [Spec-decoding lesson]  "Speculative decoding and EAGLE"
+ *                    (ai-engineering.com.cn): sections "Concept" (K+1 positions,
+ *                    bonus token), "Exactness rule" (accept iff r < p(x)/q(x),
+ *                    else sample (p-q)+ normalised; greedy: accept iff
+ *                    argmax(p) == x) and "Tree-attention verification".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller (any device
+ *    allocator).  Structs are HOST structs, read during the call and not kept.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on that stream: it never allocates, frees
+ *    or synchronises, and returns as soon as the work is queued.
+ *  - Return value: SV_OK (0) or a negative sv_status.  Problems visible from
+ *    the host (null pointers, bad sizes, a workspace that is too small,
+ *    unsupported shapes) are reported before anything is launched; a launch
+ *    failure returns SV_E_HIP.  sv_last_error() gives a detail string for the
+ *    calling thread.
+ *  - Problems in the data (a malformed tree, a token outside the vocabulary,
+ *    a non-finite target logit) are per sequence: they are reported on the
+ *    device in tree_status[b] (SV_TREE_*), and that sequence's outputs are
+ *    written as zeros / -1 / count 0.  Other sequences are unaffected.
+ *  - Flattened trees: position 0 of every sequence is the root (the last
+ *    emitted token, verified in the same pass); positions 1..T_b-1 are the
+ *    draft nodes in an order where every parent precedes its children
+ *    (parent[i] < i).  Siblings are tried in increasing position, which must
+ *    be the order the drafter drew them in.
+ *  - Limits: 1 <= T_max <= 256; D in {64, 128}; Hq % Hkv == 0; V >= 1.
+ */
+#ifndef SV_H_
+#define SV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sv_status;
+
+/* Host-side return codes. */
+enum {
+  SV_OK = 0,
+  SV_E_NULL = -1,        /* a required pointer is NULL                              */
+  SV_E_SHAPE = -2,       /* a size is out of range or inconsistent                  */
+  SV_E_DTYPE = -3,       /* unknown dtype code                                      */
+  SV_E_WORKSPACE = -4,   /* ws_bytes < sv_workspace_bytes(...) or ws misaligned     */
+  SV_E_HIP = -5,         /* a HIP runtime call or kernel launch failed              */
+  SV_E_UNSUPPORTED = -6  /* valid but not supported (T_max > 256, D not 64/128, ...) */
+};
+
+/* Per-sequence device-side status (tree_status[b]). */
+enum {
+  SV_TREE_OK = 0,
+  SV_TREE_E_ROOT = 1,      /* parent[b][0] != -1                                      */
+  SV_TREE_E_PARENT = 2,    /* some 1 <= i < T_b has parent[b][i] outside [0, i)       */
+  SV_TREE_E_COUNT = 3,     /* num_nodes[b] outside [1, T_max]                         */
+  SV_TREE_E_TOKEN = 4,     /* some tokens[b][i], i < T_b, outside [0, V)              */
+  SV_TREE_E_NONFINITE = 5, /* a NaN or +-Inf in target_logits[b][0..T_b)              */
+  SV_TREE_E_NOQ = 6,       /* temperature[b] > 0 but q_probs is NULL                  */
+  SV_TREE_E_SYNC = 7       /* internal: a cross-workgroup wait timed out              */
+};
+
+/* Element types. */
+enum { SV_F32 = 0, SV_BF16 = 1 };
+
+/* How the siblings of one node were drafted (decides the proposal each of
+ * them is tested against, see sv_spec_accept). */
+enum { SV_SIB_WITHOUT_REPLACEMENT = 0, SV_SIB_IID = 1 };
+
+/* Flattened draft trees of a batch. */
+typedef struct {
+  int32_t B;                /* sequences, >= 0                                        */
+  int32_t T_max;            /* padded positions per sequence (root + draft nodes)     */
+  const int32_t* parent;    /* [B][T_max]; parent[b][0] = -1, 0 <= parent[b][i] < i   */
+  const int32_t* num_nodes; /* [B]; T_b = root + draft nodes, 1 <= T_b <= T_max       */
+  const int32_t* tokens;    /* [B][T_max]; token of each position (root's is unused)  */
+} sv_tree;
+
+/* Tree attention inputs (post-RoPE projections of one layer). */
+typedef struct {
+  int32_t Hq, Hkv, D;       /* query heads, KV heads (Hq % Hkv == 0), head dim          */
+  int32_t L_max;            /* capacity of the cache's length axis (>= max L_b)         */
+  int32_t dtype;            /* SV_F32 or SV_BF16, for q, k_new, v_new, caches and out   */
+  float scale;              /* score scale; <= 0 means 1/sqrt(D)                        */
+  const void* q;            /* [B][T_max][Hq][D]  queries of the tree positions         */
+  const void* k_new;        /* [B][T_max][Hkv][D] keys of the tree positions            */
+  const void* v_new;        /* [B][T_max][Hkv][D] values of the tree positions          */
+  const void* k_cache;      /* [B][Hkv][L_max][D] prefix keys (read only)               */
+  const void* v_cache;      /* [B][Hkv][L_max][D] prefix values (read only)             */
+  const int32_t* prefix_len;/* [B]; L_b in [0, L_max] (a sequence outside: zero output)   */
+  void* out;                /* [B][T_max][Hq][D]; rows i >= T_b written as 0            */
+} sv_attn_args;
+
+/* Accept / reject inputs and outputs. */
+typedef struct {
+  int32_t V;                 /* vocabulary size                                          */
+  int32_t logit_dtype;       /* SV_F32 or SV_BF16 for target_logits                      */
+  int32_t sibling_mode;      /* SV_SIB_WITHOUT_REPLACEMENT or SV_SIB_IID                 */
+  const void* target_logits; /* [B][T_max][V]; row n = target logits for the token
+                                following position n                                      */
+  const float* q_probs;      /* [B][T_max][V]; row n = draft distribution n's children
+                                were drawn from (already at temperature).  May be NULL
+                                when every temperature is 0.                              */
+  const float* temperature;  /* [B]; 0 selects greedy verification for that sequence     */
+  const float* u_accept;     /* [B][T_max] in [0,1): uniform for testing candidate i     */
+  const float* u_sample;     /* [B][T_max] in [0,1): uniform for the draw at terminal n  */
+  int32_t* out_tokens;       /* [B][T_max]; accepted tokens then the drawn one, -1 pad   */
+  int32_t* out_nodes;        /* [B][T_max]; accepted positions (root excluded), -1 pad   */
+  int32_t* out_count;        /* [B]; accepted + 1 (0 for an invalid sequence)            */
+  int32_t* out_passes;       /* [B] or NULL: vocabulary passes the walk made             */
+} sv_accept_args;
+
+/* Ancestor-or-self mask of every tree, plus node depths and the validity of
+ * each tree ([EAGLE article] sec. 2.3 "Flatten + Attention mask";
+ * [Spec-decoding lesson] "Tree-attention verification").
+ *   anc         [B][T_max][W] uint64, W = ceil(T_max / 64): bit (j % 64) of
+ *               word j / 64 of row i is set iff j == i or j is an ancestor of i.
+ *               Rows and bits >= T_b, and all rows of an invalid tree, are 0.
+ *   depth       [B][T_max] int32: edges from the root (0 for padding/invalid).
+ *   tree_status [B] int32: SV_TREE_OK, _ROOT, _PARENT or _COUNT (written).
+ * Needs no workspace. */
+sv_status sv_tree_mask_build(const sv_tree* tree, uint64_t* anc, int32_t* depth,
+                             int32_t* tree_status, void* stream);
+
+/* Tree attention ([EAGLE article] sec. 1.3 "Verification";
+ * [Spec-decoding lesson] "Tree-attention verification"): for every sequence b
+ * with tree_status[b] == 0, position i < T_b and query head h, attend with
+ * softmax(scale * q.k) over the first L_b cache entries of KV head
+ * h / (Hq / Hkv) and over the tree positions j whose bit is set in anc[b][i].
+ * Accumulation is fp32; out is written in `dtype`.  Rows of invalid sequences
+ * and rows i >= T_b are written as zeros.
+ *   anc, tree_status: as produced by sv_tree_mask_build (read only).
+ *   ws / ws_bytes: device workspace of at least sv_workspace_bytes(tree, a, NULL)
+ *   bytes, 256-byte aligned (may be NULL when that size is 0). */
+sv_status sv_tree_attn(const sv_tree* tree, const uint64_t* anc, const int32_t* tree_status,
+                       const sv_attn_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* Speculative accept / reject over each tree ([Spec-decoding lesson]
+ * "Exactness rule", "Concept"; [EAGLE article] sec. 1.3, Figure 1-6).
+ * For sequence b (tree_status[b] == 0 on entry), starting at the root:
+ *   - p_n = softmax(target_logits[b][n] / temperature[b]) (float32 on device);
+ *   - greedy (temperature 0): the first child whose token equals
+ *     argmax(target_logits[b][n]) (lowest index on ties) is accepted and the
+ *     walk continues there; otherwise argmax is emitted and the walk stops;
+ *   - stochastic: children are tested in increasing position.  Candidate c
+ *     with token x is accepted iff u_accept[b][c] < P(x) / q_c(x), where P is
+ *     the current target (p_n, then the normalised residual) and q_c is the
+ *     proposal x was drawn from: q_n with the earlier siblings' tokens removed
+ *     and renormalised (SV_SIB_WITHOUT_REPLACEMENT) or q_n itself (SV_SIB_IID).
+ *     On rejection P becomes max(0, P - q_c) normalised.  When all children
+ *     are rejected, or n is a leaf (bonus token, P = p_n), the emitted token is
+ *     the smallest v with sum_{w<=v} P(w) > u_sample[b][n].
+ * Outputs: out_nodes = accepted positions, out_tokens = their tokens followed
+ * by the emitted token, out_count = accepted + 1.  tree_status[b] may be set to
+ * SV_TREE_E_TOKEN, _NONFINITE, _NOQ or _SYNC (then outputs are -1 / count 0).
+ *   ws / ws_bytes: at least sv_workspace_bytes(tree, NULL, a) bytes, 256-byte
+ *   aligned.  The walk kernel is a cooperative launch; calls that overlap on
+ *   one device must use different workspaces. */
+sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_accept_args* a,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* One verification step: sv_tree_mask_build, then sv_tree_attn, then
+ * sv_spec_accept, in stream order, sharing one workspace of at least
+ * sv_workspace_bytes(tree, attn, acc) bytes. */
+sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
+                         uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by sv_tree_attn (attn != NULL), sv_spec_accept
+ * (acc != NULL) or both (the maximum).  Host only; reads only the scalar
+ * fields of the structs.  Returns 0 on invalid sizes (see sv_last_error). */
+size_t sv_workspace_bytes(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc);
+
+/* Static description of a status code (host or tree status). */
+const char* sv_status_string(sv_status s);
+
+/* Detail of the last host-side error on the calling thread ("" if none). */
+const char* sv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SV_H_ */

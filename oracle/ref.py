@@ -23,14 +23,15 @@ in the design notes of the repository):
 * the tree mask is ancestor-or-self;
 * attention scale 1/sqrt(D) unless given; query head h reads KV head
   floor(h / (Hq / Hkv));
-* p = softmax(z / tau); tau = 0 means greedy; ties break to the lowest index;
+* p = softmax(z / tau); tau <= 0 means greedy; ties break to the lowest index;
 * sibling candidates are tested in increasing node index with the residual
   updated after each rejection; the proposal of the i-th sibling is q with the
   earlier siblings' tokens removed and renormalised when siblings were drawn
   without replacement, and q itself when drawn i.i.d.;
 * the terminal draw is an inverse CDF in ascending token order;
-* a non-finite target logit in rows 0..T_b-1, or a token outside [0, V), marks
-  the sequence invalid (count 0, outputs -1).
+* a non-finite target logit in rows 0..T_b-1, a token outside [0, V), or a
+  stochastic sequence without draft probabilities marks the sequence invalid
+  (count 0, outputs -1).
 
 Parity is pinned by the tests under ``tests/test_oracle_*.py`` (closed forms,
 the worked example trees and numbers the pages print, library routines for the
@@ -46,6 +47,7 @@ TREE_E_PARENT = 2
 TREE_E_COUNT = 3
 TREE_E_TOKEN = 4
 TREE_E_NONFINITE = 5
+TREE_E_NOQ = 6
 
 SIB_WITHOUT_REPLACEMENT = 0
 SIB_IID = 1
@@ -248,7 +250,7 @@ def accept_walk(parent_row, tokens_row, T_b, zrow, qrow, tau, u_accept_row, u_sa
     children = {n: [] for n in range(T_b)}
     for i in range(1, T_b):
         children[int(parent_row[i])].append(i)   # increasing index order
-    greedy = float(np.float32(tau)) == 0.0
+    greedy = not (float(np.float32(tau)) > 0.0)   # tau <= 0 (or NaN) selects greedy
     path, decisions = [], []
     passes = 0
     exempt_at = None
@@ -339,6 +341,9 @@ def spec_accept(parent, num_nodes, tokens, target_logits, logit_dtype, q_probs, 
                       for n in range(T_b))
         if not rows_ok:
             status[b] = TREE_E_NONFINITE
+            continue
+        if q_probs is None and float(np.float32(temperature[b])) > 0.0:
+            status[b] = TREE_E_NOQ      # stochastic verification needs the draft distribution
             continue
         w = accept_walk(parent[b], tokens[b], T_b,
                         lambda n, b=b: to_f64(target_logits[b, n], logit_dtype),

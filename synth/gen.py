@@ -206,7 +206,11 @@ def make_instance(spec, seed=0, with_attn=True, with_accept=True):
         inst.target_logits = np.empty((B, T_max, V),
                                       dtype=np.uint16 if logit_dtype == "bf16" else np.float32)
         inst.q_probs = np.empty((B, T_max, V), dtype=np.float32)
-    for b in range(B):
+    if not with_accept:
+        # no logits: draft tokens are uniform (only the tree shape matters)
+        for b in range(B):
+            tokens[b, :int(num_nodes[b])] = r_draft.integers(0, V, size=int(num_nodes[b]))
+    for b in (range(B) if with_accept else []):
         zq = r_logits.standard_normal(size=(T_max, V), dtype=np.float32) * np.float32(draft_std)
         noise = r_logits.standard_normal(size=(T_max, V), dtype=np.float32) * np.float32(sigma)
         zp = zq + noise
@@ -219,9 +223,8 @@ def make_instance(spec, seed=0, with_attn=True, with_accept=True):
         z64 /= z64.sum(axis=1, keepdims=True)
         q32 = z64.astype(np.float32)
         del z64
-        if with_accept:
-            inst.target_logits[b] = bf16_bits_from_f32(zp) if logit_dtype == "bf16" else zp
-            inst.q_probs[b] = q32
+        inst.target_logits[b] = bf16_bits_from_f32(zp) if logit_dtype == "bf16" else zp
+        inst.q_probs[b] = q32
         # draft tokens
         Tb = int(num_nodes[b])
         tokens[b, 0] = int(r_draft.integers(0, V))

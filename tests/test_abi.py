@@ -1,0 +1,116 @@
+"""The C-ABI library: it loads, exports every entry point include/sv.h
+declares, mirrors the header's constants, and rejects bad host arguments
+before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import eagle_tree_verification_attn_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:sv_status|size_t|const char\*)\s+(sv_\w+)\(", text, re.M)))
+
+
+def _enums():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(SV_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert names == sorted(sv.EXPORTS)
+    L = ctypes.CDLL(sv.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", sv.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(r"\bT " + n + r"\b", dyn), n
+
+
+def test_binding_constants_match_header():
+    for k, v in _enums().items():
+        assert getattr(sv, k) == v, k
+
+
+def test_status_strings():
+    for code in list(range(-6, 1)) + list(range(1, 8)):
+        s = sv.sv_status_string(code)
+        assert s and s != "unknown status"
+    assert sv.sv_status_string(99) == "unknown status"
+
+
+def _tree(B=2, T=5):
+    fake = ctypes.c_void_p(0x1000)
+    t = sv.SvTree(B, T, fake, fake, fake)
+    return t
+
+
+def _attn(**kw):
+    fake = 0x10000
+    a = sv.SvAttnArgs(8, 2, 64, 16, sv.SV_BF16, 0.0, fake, fake, fake, fake, fake, fake, fake)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _acc(**kw):
+    fake = 0x10000
+    a = sv.SvAcceptArgs(1000, sv.SV_BF16, 0, fake, fake, fake, fake, fake, fake, fake, fake, None)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_host_validation_rejects_before_launch():
+    L = sv.lib()
+    null = None
+    fake = ctypes.c_void_p(0x10000)
+    assert L.sv_tree_mask_build(null, fake, fake, fake, null) == sv.SV_E_NULL
+    assert L.sv_tree_mask_build(ctypes.byref(_tree(T=0)), fake, fake, fake, null) == sv.SV_E_SHAPE
+    assert L.sv_tree_mask_build(ctypes.byref(_tree(T=257)), fake, fake, fake, null) == sv.SV_E_UNSUPPORTED
+    assert L.sv_tree_mask_build(ctypes.byref(_tree(B=-1)), fake, fake, fake, null) == sv.SV_E_SHAPE
+    assert L.sv_tree_mask_build(ctypes.byref(_tree()), null, fake, fake, null) == sv.SV_E_NULL
+    t = ctypes.byref(_tree())
+    assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(Hkv=3)), fake, 1 << 30, null) == sv.SV_E_SHAPE
+    assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(D=96)), fake, 1 << 30, null) == sv.SV_E_UNSUPPORTED
+    assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(dtype=7)), fake, 1 << 30, null) == sv.SV_E_DTYPE
+    assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(q=None)), fake, 1 << 30, null) == sv.SV_E_NULL
+    assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(q=0x10008)), fake, 1 << 30, null) == sv.SV_E_UNSUPPORTED
+    assert L.sv_spec_accept(t, fake, ctypes.byref(_acc(V=0)), fake, 1 << 30, null) == sv.SV_E_SHAPE
+    assert L.sv_spec_accept(t, fake, ctypes.byref(_acc(logit_dtype=5)), fake, 1 << 30, null) == sv.SV_E_DTYPE
+    assert L.sv_spec_accept(t, fake, ctypes.byref(_acc(sibling_mode=2)), fake, 1 << 30, null) == sv.SV_E_SHAPE
+    assert L.sv_spec_accept(t, fake, ctypes.byref(_acc(u_sample=None)), fake, 1 << 30, null) == sv.SV_E_NULL
+    assert L.sv_spec_accept(t, fake, ctypes.byref(_acc(V=2_000_000)), fake, 1 << 30, null) == sv.SV_E_UNSUPPORTED
+    # workspace: missing, too small, misaligned
+    need = L.sv_workspace_bytes(t, None, ctypes.byref(_acc()))
+    assert need > 0
+    assert L.sv_spec_accept(t, fake, ctypes.byref(_acc()), None, need, null) == sv.SV_E_WORKSPACE
+    assert L.sv_spec_accept(t, fake, ctypes.byref(_acc()), fake, need - 1, null) == sv.SV_E_WORKSPACE
+    assert L.sv_spec_accept(t, fake, ctypes.byref(_acc()), ctypes.c_void_p(0x10010), need, null) == sv.SV_E_WORKSPACE
+    assert "workspace" in sv.sv_last_error()
+    # an empty batch is valid and launches nothing
+    empty = sv.SvTree(0, 4, None, None, None)
+    assert L.sv_tree_mask_build(ctypes.byref(empty), None, None, None, null) == sv.SV_OK
+    assert sv.sv_last_error() == ""
+
+
+def test_workspace_sizes_for_the_workloads():
+    from synth import CONFIGS
+    for c in CONFIGS:
+        T = 130 if c["tree"][0] == "dynamic" else 1 + (c["tree"][1] if c["tree"][0] == "chain" else sum(c["tree"][1]))
+        t = sv.SvTree(c["B"], T, None, None, None)
+        a = _attn(Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"], L_max=c["prefix_len"],
+                  dtype=sv.SV_BF16 if c["dtype"] == "bf16" else sv.SV_F32)
+        acc = _acc(V=c["V"])
+        n_acc = sv.sv_workspace_bytes(t, None, acc)
+        n_both = sv.sv_workspace_bytes(t, a, acc)
+        assert n_acc > 0 and n_both >= n_acc
+        assert n_both % 256 == 0

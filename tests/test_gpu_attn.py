@@ -1,0 +1,128 @@
+"""GPU tree attention (sv_tree_attn) against the float64 oracle.
+
+Small cases are compared element by element (several key blocks, ragged
+prefixes including 0, ragged trees, T_b = 1, every instantiated kernel shape,
+forced key splits, fp32 and bf16).  The five workload shapes run at full size
+in the launch configuration the benchmark uses and are compared on sampled
+(sequence, head) units the oracle computes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check_attention, need_gpu, say, sv_problem
+from synth import CONFIGS, make_instance
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(**kw):
+    s = dict(cfg_id=100, B=2, Hq=8, Hkv=2, D=128, dtype="bf16", logit_dtype="bf16", prefix_len=64,
+             tree=("widths", [2, 3]), V=64, tau=1.0, sigma=1.0, draft_std=3.0, sibling_mode="wor")
+    s.update(kw)
+    return s
+
+
+def _run(inst, label, env=None, rows=None):
+    old = {}
+    for k, v in (env or {}).items():
+        old[k] = os.environ.get(k)
+        os.environ[k] = v
+    try:
+        say(f"attn {label} B={inst.B} Hq={inst.Hq} Hkv={inst.Hkv} D={inst.D} T_max={inst.T_max} "
+            f"L={inst.prefix_len.tolist()} env={env}")
+        dev = sv_problem(inst, with_accept=False)
+        dev.mask_build()
+        dev.tree_attn()
+        got = dev.attn_result()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    anc, _, _, status = oracle.tree_mask(inst.parent, inst.num_nodes, inst.T_max)
+    ref = oracle.tree_attention(inst.q, inst.k_new, inst.v_new, inst.k_cache, inst.v_cache,
+                                inst.prefix_len, anc, inst.num_nodes, status, inst.dtype, units=rows)
+    err = check_attention(got, ref, inst.dtype, rows=rows, label=label)
+    # rows past each tree are exactly zero
+    for b in range(inst.B):
+        assert not got[b, int(inst.num_nodes[b]):].any()
+    return err
+
+
+SMALL = {
+    "bf16_g8_d128_ragged": _spec(B=3, Hq=16, Hkv=2, prefix_len=[0, 77, 300],
+                                 tree=("dynamic", 1, 5, 1, 6, 1, 40), T_max=48),
+    "bf16_g8_d64_ragged": _spec(B=3, Hq=16, Hkv=2, D=64, prefix_len=[513, 64, 1],
+                                tree=("dynamic", 1, 6, 1, 8, 1, 60)),
+    "bf16_chain_g4": _spec(B=4, Hq=8, Hkv=2, prefix_len=[2048, 100, 31, 0], tree=("chain", 4)),
+    "bf16_decode_T1": _spec(B=3, Hq=4, Hkv=4, prefix_len=[1, 250, 1000], tree=("chain", 0)),
+    "bf16_g5_d128": _spec(B=2, Hq=10, Hkv=2, prefix_len=[333, 1200], tree=("widths", [4, 8, 8])),
+    "bf16_g1_d64": _spec(B=2, Hq=3, Hkv=3, D=64, prefix_len=[95, 96], tree=("widths", [2, 2, 2])),
+    "bf16_long_prefix": _spec(B=1, Hq=8, Hkv=1, prefix_len=5000, tree=("widths", [3, 4, 5])),
+    "f32_tiny": _spec(B=1, Hq=4, Hkv=4, D=64, dtype="f32", prefix_len=128, tree=("widths", [2, 4, 4])),
+    "f32_g5_d128_ragged": _spec(B=3, Hq=10, Hkv=2, dtype="f32", prefix_len=[0, 200, 700],
+                                tree=("dynamic", 1, 4, 1, 5, 1, 30)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_attention_small(name):
+    need_gpu()
+    inst = make_instance(SMALL[name], 1, with_accept=False)
+    _run(inst, name)
+
+
+@pytest.mark.parametrize("variant", ["3,4", "2,4", "2,1", "1,1"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_attention_every_kernel_shape(variant, D):
+    need_gpu()
+    if D == 64:
+        variant = {"3,4": "4,4", "2,4": "3,4"}.get(variant, variant)
+    spec = _spec(B=2, Hq=16, Hkv=2, D=D, prefix_len=[190, 411], tree=("dynamic", 2, 5, 2, 8, 10, 45))
+    inst = make_instance(spec, 2, with_accept=False)
+    _run(inst, f"shape D={D} {variant}", env={"SV_ATTN_VARIANT": variant})
+
+
+@pytest.mark.parametrize("lsplit", [2, 3, 7])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_key_splits(lsplit, dtype):
+    need_gpu()
+    spec = _spec(B=2, Hq=8, Hkv=2, dtype=dtype, prefix_len=[700, 33], tree=("widths", [3, 3, 3]))
+    inst = make_instance(spec, 3, with_accept=False)
+    _run(inst, f"lsplit={lsplit} {dtype}", env={"SV_ATTN_LSPLIT": str(lsplit)})
+
+
+def test_attention_invalid_sequences_zero():
+    need_gpu()
+    spec = _spec(B=3, prefix_len=[50, 60, 70], tree=("widths", [2, 2]))
+    inst = make_instance(spec, 4, with_accept=False)
+    inst.parent[1, 2] = 5          # parent not before its child
+    inst.prefix_len[2] = 10_000    # beyond the cache
+    say("attn invalid sequences")
+    dev = sv_problem(inst, with_accept=False)
+    dev.mask_build()
+    dev.tree_attn()
+    got = dev.attn_result()
+    assert np.abs(got[0]).sum() > 0
+    assert not got[1].any() and not got[2].any()
+
+
+def _sample_units(inst, n=6):
+    rng = np.random.default_rng(0)
+    units = {(0, 0), (inst.B - 1, inst.Hq - 1)}
+    while len(units) < n:
+        units.add((int(rng.integers(0, inst.B)), int(rng.integers(0, inst.Hq))))
+    return sorted(units)
+
+
+@pytest.mark.parametrize("cfg", [c["name"] for c in CONFIGS])
+def test_attention_full_workloads_sampled(cfg):
+    need_gpu()
+    spec = dict(next(c for c in CONFIGS if c["name"] == cfg))
+    inst = make_instance(spec, 0, with_accept=False)
+    rows = None if spec["cfg_id"] == 1 else _sample_units(inst)
+    _run(inst, f"full {cfg}", rows=rows)
