@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Tree-verification benchmark on one MI355X.
+
+One step = sv_verify_step (tree mask -> tree attention -> per-node target
+softmax statistics -> accept / reject walk) over one batch of the
+Llama-3-70B-shaped workload: 32 sequences, 64 query / 8 KV heads, head dim 128,
+KV prefix 8192, a 64-node draft tree of depth 6, vocabulary 128256,
+temperature 0.8, bf16.  Inputs are synthetic (seeded), generated on the host
+and resident in HBM before timing starts.
+
+Prints one JSON line: steps/s, ms per step, per-kernel times (HIP events on
+the launch stream), the roofline of the dominant kernel, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+    python bench.py --kernels-only   (for rocprofv3 runs: kernels + a copy of known size)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify steps/sec (attn+accept) and % HBM roofline, B=32 70B-shape"
+WORKLOAD = "tree64_llama70b_b32"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+COUNTERS = os.path.join(ROOT, "profiles", "tree_attn_tree64_llama70b_b32_counters.json")
+ATTN_SRC = os.path.join(ROOT, "eagle_tree_verification_attn_amd", "csrc", "attn.hip")
+
+
+def algorithmic_work(inst):
+    """Algorithmic attention flops / bytes and accept bytes of one step.
+
+    Attention: 4 * D flops per (query head, visible key) pair -- QK^T and PV --
+    over L_b prefix keys plus depth+1 ancestor keys per position; bytes = the
+    prefix K and V once, Q in, O out, tree K/V once, mask words.
+    Accept (statistics pass): every logits row of every position once.
+    """
+    import numpy as np
+    import oracle  # noqa: F401  (the oracle's mask gives the depths)
+    s = 2 if inst.dtype == "bf16" else 4
+    sz = 2 if inst.logit_dtype == "bf16" else 4
+    _, _, depth, _ = oracle.tree_mask(inst.parent, inst.num_nodes, inst.T_max)
+    pairs = 0
+    for b in range(inst.B):
+        T = int(inst.num_nodes[b])
+        pairs += T * int(inst.prefix_len[b]) + int((depth[b, :T] + 1).sum())
+    flops = 4.0 * inst.Hq * inst.D * pairs
+    W = (inst.T_max + 63) // 64
+    attn_bytes = float(s * (2 * inst.Hkv * inst.D * int(inst.prefix_len.sum())
+                            + 2 * inst.Hq * inst.D * int(inst.num_nodes.sum())
+                            + 2 * inst.Hkv * inst.D * int(inst.num_nodes.sum()))
+                       + 8 * inst.B * inst.T_max * W)
+    stats_bytes = float(sz * inst.V * int(inst.num_nodes.sum()))
+    return flops, attn_bytes, stats_bytes
+
+
+def time_launches(fn, n, stream):
+    """Average duration (ms) of n calls of fn, HIP events on the launch stream."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def counters_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    try:
+        info = json.load(open(COUNTERS))
+        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if info.get("attn_source_sha256") != src:
+            return None
+        return float(info["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(inst, seconds):
+    """The oracle on a bounded sample: whole sequences (attention for all heads,
+    target softmax and walk), scaled to steps/s of the full batch."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    anc, _, _, status = oracle.tree_mask(inst.parent, inst.num_nodes, inst.T_max)
+    done, t0 = 0, time.perf_counter()
+    while done < inst.B:
+        b = done
+        oracle.tree_attention(inst.q, inst.k_new, inst.v_new, inst.k_cache, inst.v_cache,
+                              inst.prefix_len, anc, inst.num_nodes, status, inst.dtype,
+                              units=[(b, h) for h in range(inst.Hq)])
+        oracle.spec_accept(inst.parent, inst.num_nodes, inst.tokens, inst.target_logits,
+                           inst.logit_dtype, inst.q_probs, inst.temperature, inst.u_accept,
+                           inst.u_sample, status, seqs=[b])
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    per_step = dt * inst.B / done
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {inst.B} sequences (all heads' attention, softmax, walk) in "
+                      f"{dt:.1f} s, scaled to the batch"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="launch the kernels a few times plus a 1 GiB copy (for rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(sequences shard across GPUs with no communication: run one process per GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import eagle_tree_verification_attn_amd as sv
+    from eagle_tree_verification_attn_amd.problem import DeviceProblem
+    from synth import config_by_name, make_instance
+
+    sv.lib()   # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    cfg = config_by_name(args.config)
+    t0 = time.perf_counter()
+    inst = make_instance(cfg, 0)
+    gen_s = time.perf_counter() - t0
+    dev = DeviceProblem(inst, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    print(f"bench: {cfg['name']} generated in {gen_s:.1f} s, uploaded", file=sys.stderr, flush=True)
+
+    if args.kernels_only:
+        for _ in range(3):
+            dev.verify_step()
+        for _ in range(5):
+            dev.tree_attn()
+        for _ in range(5):
+            dev.spec_accept()
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench: kernels-only done (copy size 1073741824 bytes)", file=sys.stderr, flush=True)
+        return
+
+    for _ in range(args.warmup):
+        dev.verify_step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        dev.verify_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    print(f"bench: {args.steps} steps, {ms_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
+          file=sys.stderr, flush=True)
+
+    n = max(10, args.steps)
+    mask_ms = time_launches(dev.mask_build, n, stream)
+    attn_ms = time_launches(dev.tree_attn, n, stream)
+    acc_ms = time_launches(dev.spec_accept, n, stream)
+    res = dev.accept_results()
+    flops, attn_bytes, stats_bytes = algorithmic_work(inst)
+
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
+    # accept bytes: every logits row once, plus one (logits row, q row) read per
+    # vocabulary pass of the walk
+    sz = 2 if inst.logit_dtype == "bf16" else 4
+    walk_bytes = float(int(res["out_passes"].sum()) * inst.V * (sz + 4))
+    acc_bytes = stats_bytes + walk_bytes
+    acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
+    traffic = counters_traffic()
+    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "k_attn_bf16 (sv_tree_attn)",
+                "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(attn_ms, 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inst, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "B": cfg["B"], "Hq": cfg["Hq"], "Hkv": cfg["Hkv"],
+                   "D": cfg["D"], "prefix_len": cfg["prefix_len"], "tree_nodes": int(inst.num_nodes[0]) - 1,
+                   "depth": 6, "V": cfg["V"], "temperature": cfg["tau"], "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_ms": {"tree_mask_build": round(mask_ms, 5), "tree_attn": round(attn_ms, 5),
+                       "spec_accept": round(acc_ms, 5)},
+        "hbm_roofline": {"tree_attn_verify": {"algorithmic_bytes": attn_bytes,
+                                              "GB_s": round(attn_gbs, 1),
+                                              "frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
+                         "tree_spec_accept": {"algorithmic_bytes": acc_bytes,
+                                              "GB_s": round(acc_gbs, 1),
+                                              "frac": round(acc_gbs / HBM_PEAK_GBS, 4)}},
+        "emitted_tokens_per_seq": round(float(np.mean(res["out_count"])), 3),
+        "vocab_passes_per_seq": round(float(np.mean(res["out_passes"])), 3),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

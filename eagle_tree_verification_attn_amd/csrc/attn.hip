@@ -17,9 +17,10 @@
 //   softmax  online, fp32, exp2 with the scale folded in; the running max is
 //            only raised when a block's max exceeds it by more than 8 (log2
 //            units), so the O rescale is rare and exp2 arguments stay <= 8;
-//   output   O^T[d][row] += V^T[d][key] P^T[key][row], A = V^T from LDS (V is
-//            transposed on its way into LDS), B = P taken straight from the
-//            score registers (same key permutation on both operands).
+//   output   O^T[d][row] += V^T[d][key] P^T[key][row]: B = P taken straight
+//            from the score registers; A = V^T read from the row-major V tile
+//            with ds_read_b64_tr_b16 (each 16-lane group gathers 4 keys x 16
+//            dims and gets them transposed), in the same key permutation.
 //
 // Keys of one (b, KV head) are numbered 0 .. L_b + T_b - 1: first the cache
 // prefix, then the tree tokens; keys >= L_b are visible to row (t, g) iff bit
@@ -77,23 +78,34 @@ __device__ inline float wave_sum16_32(float v) {
   return v;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte staging unit
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i % 4) of the 8-byte rows addressed by lanes 4k + i / 4, k = 0..3.
+__device__ inline bf16x4 lds_read_tr16(const __bf16* p) {
+  typedef __bf16 __attribute__((address_space(3))) lds_bf16;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)(
+      (lds_bf16*)(p)));
 }
 
 template <int D, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_bf16(AttnParams p) {
   constexpr int NTHR = NW * 64;
-  constexpr int KS = D + 8;    // LDS row stride (elements) of the K tile  [BK][KS]
-  constexpr int VS = BK + 4;   // LDS row stride (elements) of the V^T tile [D][VS]
+  constexpr int KS = D + 8;    // LDS row stride (elements) of the K and V tiles [BK][KS]
   constexpr int K_ELEMS = BK * KS;
-  constexpr int V_ELEMS = D * VS;
-  constexpr int STAGE = K_ELEMS + V_ELEMS;
-  constexpr int KCH = BK * D / 8;         // 16-byte K chunks per block
-  constexpr int VUN = (BK / 2) * (D / 8); // V units (2 keys x 8 dims) per block
+  constexpr int STAGE = 2 * K_ELEMS;      // K tile then V tile
+  constexpr int KCH = BK * D / 8;         // 16-byte chunks per tile
   constexpr int KPT = (KCH + NTHR - 1) / NTHR;
-  constexpr int VPT = (VUN + NTHR - 1) / NTHR;
+  static_assert(KCH % NTHR == 0 || NTHR > KCH, "chunk split");  // extra threads repeat chunks
   constexpr int DK = D / 32;              // MFMA k-steps over the head dim
   constexpr int DT = D / 16;              // 16-row output tiles over the head dim
 
@@ -132,6 +144,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const __bf16* kn = reinterpret_cast<const __bf16*>(p.k_new) + ((size_t)b * p.T_max * p.Hkv + kvh) * D;
   const __bf16* vn = reinterpret_cast<const __bf16*>(p.v_new) + ((size_t)b * p.T_max * p.Hkv + kvh) * D;
   const size_t new_stride = (size_t)p.Hkv * D;  // elements between consecutive tree tokens
+  const uint32_t new_stride32 = (uint32_t)new_stride;
 
   // rows owned by this lane (one per 16-row tile)
   int rrow[NT];
@@ -201,33 +214,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- staging of one key block: global -> registers -> LDS
-  uint4 kst[KPT];
-  uint4 vst[VPT][2];
-  auto key_src = [&](int j, const __bf16* cache, const __bf16* tree) -> const __bf16* {
-    return j < Lb ? cache + (size_t)j * D : tree + (size_t)(j - Lb) * new_stride;
-  };
+  // ---- staging of one key block: global -> registers -> LDS.  Thread chunk
+  // i covers key (id / (D/8)), dims [8 * (id % (D/8)), +8) of the block, for
+  // K and V alike.  Every load is unconditional and branch-free (so the next
+  // block's loads stay in flight across the whole iteration): each key picks
+  // its source (cache prefix or tree token), and keys past the range end are
+  // clamped to the last valid key (their scores are masked to -inf, so those
+  // rows of V are weighted by exactly 0).
+  u32x4 kst[KPT], vst[KPT];
+  int ckey[KPT], cseg[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int id = (tid + i * NTHR) % KCH;
+    ckey[i] = id / (D / 8);
+    cseg[i] = id % (D / 8);
+  }
   auto load_block = [&](int blk) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int id = tid + i * NTHR;
-      kst[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (id < KCH) {
-        const int key = id / (D / 8), seg = id % (D / 8);
-        const int j = blk + key;
-        if (j < kend) kst[i] = *reinterpret_cast<const uint4*>(key_src(j, kc, kn) + seg * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int id = tid + i * NTHR;
-      vst[i][0] = vst[i][1] = make_uint4(0u, 0u, 0u, 0u);
-      if (id < VUN) {
-        const int kp = id % (BK / 2), ds = id / (BK / 2);
-        const int j = blk + 2 * kp;
-        if (j < kend) vst[i][0] = *reinterpret_cast<const uint4*>(key_src(j, vc, vn) + ds * 8);
-        if (j + 1 < kend) vst[i][1] = *reinterpret_cast<const uint4*>(key_src(j + 1, vc, vn) + ds * 8);
-      }
+      const int jr = blk + ckey[i];
+      const int j = jr < kend ? jr : kend - 1;
+      const bool in_cache = j < Lb;
+      // 32-bit element offset inside the selected source; no branches, so
+      // the loads of one block are issued back to back
+      const uint32_t loc = in_cache ? (uint32_t)j * D : (uint32_t)(j - Lb) * new_stride32;
+      const __bf16* kb = in_cache ? kc : kn;
+      const __bf16* vb = in_cache ? vc : vn;
+      kst[i] = *reinterpret_cast<const u32x4*>(kb + loc + cseg[i] * 8);
+      vst[i] = *reinterpret_cast<const u32x4*>(vb + loc + cseg[i] * 8);
     }
   };
   auto store_block = [&](int buf) {
@@ -235,26 +249,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __bf16* vs = ks + K_ELEMS;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int id = tid + i * NTHR;
-      if (id < KCH) {
-        const int key = id / (D / 8), seg = id % (D / 8);
-        *reinterpret_cast<uint4*>(ks + key * KS + seg * 8) = kst[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int id = tid + i * NTHR;
-      if (id < VUN) {
-        const int kp = id % (BK / 2), ds = id / (BK / 2);
-        const uint32_t* a = reinterpret_cast<const uint32_t*>(&vst[i][0]);
-        const uint32_t* bb = reinterpret_cast<const uint32_t*>(&vst[i][1]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = (e & 1) ? (a[e >> 1] >> 16) : (a[e >> 1] & 0xFFFFu);
-          const uint32_t hi = (e & 1) ? (bb[e >> 1] & 0xFFFF0000u) : (bb[e >> 1] << 16);
-          *reinterpret_cast<uint32_t*>(vs + (ds * 8 + e) * VS + 2 * kp) = lo | hi;
-        }
-      }
+      const int off = ckey[i] * KS + cseg[i] * 8;
+      *reinterpret_cast<u32x4*>(ks + off) = kst[i];
+      *reinterpret_cast<u32x4*>(vs + off) = vst[i];
     }
   };
 
@@ -346,13 +343,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       pk[qt] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T.  Lane (g, c) needs V[key][16 dt + c] for keys
+    // 4g + k and 16 + 4g + k (k = 0..3); as a source of the transposed read it
+    // addresses row 4g + c/4 (+16), dims 16 dt + 4 (c % 4) .. +3.
+    const __bf16* vsrc = vs + (4 * g + (c >> 2)) * KS + 4 * (c & 3);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const __bf16* vrow = vs + (16 * dt + c) * VS + 4 * g;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const bf16x4 lo = lds_read_tr16(vsrc + 16 * dt);
+      const bf16x4 hi = lds_read_tr16(vsrc + 16 * KS + 16 * dt);
+      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int qt = 0; qt < NT; ++qt)
         acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[qt], acc[qt][dt], 0, 0, 0);
@@ -553,7 +552,7 @@ constexpr float kRereadRows = 160.f;
 
 size_t smem_bytes(int D, int T_max) {
   const int W = (T_max + 63) / 64;
-  const size_t stage = (size_t)BK * (D + 8) + (size_t)D * (BK + 4);
+  const size_t stage = 2 * (size_t)BK * (D + 8);
   return 2 * stage * sizeof(uint16_t) + (size_t)T_max * W * sizeof(uint64_t);
 }
 }  // namespace

@@ -3,7 +3,9 @@
 Recipe (one instance per (spec, seed)):
 
 * ``SeedSequence([cfg_id, seed]).spawn(6)`` gives six independent Philox streams:
-  tree shape, tree-token Q/K/V, KV cache, logits, draft draws, uniforms.
+  tree shape, tree-token Q/K/V, KV cache, logits, draft draws, uniforms; the
+  per-sequence ones (Q/K/V, cache, logits, draft draws) have one child stream
+  per sequence.
 * Tree: nodes at depth d+1 take a parent drawn uniformly from the depth-d nodes;
   nodes are numbered by depth, then parent, then draw order, so ``parent[i] < i``
   and siblings are contiguous in the order they were drafted.
@@ -21,7 +23,10 @@ Recipe (one instance per (spec, seed)):
 Padding rows (node index >= T_b) are filled too (random values, parent -1,
 token 0); correct consumers never read them.
 """
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
+import os
+
 import numpy as np
 
 
@@ -140,14 +145,26 @@ def _draw_children(qrow64, k, mode, rng):
     return out
 
 
+def _workers():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def make_instance(spec, seed=0, with_attn=True, with_accept=True):
-    """Build one seeded instance of ``spec`` (see :mod:`synth.configs`)."""
+    """Build one seeded instance of ``spec`` (see :mod:`synth.configs`).
+
+    Per-sequence data come from child streams of each Philox stream (one child
+    per sequence), so sequences are generated in parallel threads and the
+    result does not depend on the thread count.
+    """
     s = dict(spec)
     B, Hq, Hkv, D, V = s["B"], s["Hq"], s["Hkv"], s["D"], s["V"]
     cfg_id = int(s.get("cfg_id", 0))
     ss = np.random.SeedSequence([cfg_id, int(seed)])
-    r_tree, r_qkv, r_cache, r_logits, r_draft, r_unif = [
-        np.random.Generator(np.random.Philox(c)) for c in ss.spawn(6)]
+    s_tree, s_qkv, s_cache, s_logits, s_draft, s_unif = ss.spawn(6)
+    r_tree = np.random.Generator(np.random.Philox(s_tree))
+    r_unif = np.random.Generator(np.random.Philox(s_unif))
+    child = lambda sq: [np.random.Generator(np.random.Philox(c)) for c in sq.spawn(B)]
+    r_qkv, r_cache, r_logits, r_draft = child(s_qkv), child(s_cache), child(s_logits), child(s_draft)
 
     # ---- tree shapes
     kind = s["tree"][0]
@@ -186,35 +203,39 @@ def make_instance(spec, seed=0, with_attn=True, with_accept=True):
                     parent=parent, num_nodes=num_nodes,
                     tokens=np.zeros((B, T_max), dtype=np.int32),
                     prefix_len=prefix_len, temperature=taus)
-
-    # ---- attention inputs
+    store = np.uint16 if dtype == "bf16" else np.float32
     if with_attn:
-        inst.q = _normal(r_qkv, (B, T_max, Hq, D), 1.0, dtype)
-        inst.k_new = _normal(r_qkv, (B, T_max, Hkv, D), 1.0, dtype)
-        inst.v_new = _normal(r_qkv, (B, T_max, Hkv, D), 1.0, dtype)
-        inst.k_cache = np.empty((B, Hkv, L_max, D), dtype=np.uint16 if dtype == "bf16" else np.float32)
-        inst.v_cache = np.empty_like(inst.k_cache)
-        for b in range(B):
-            inst.k_cache[b] = _normal(r_cache, (Hkv, L_max, D), 1.0, dtype)
-            inst.v_cache[b] = _normal(r_cache, (Hkv, L_max, D), 1.0, dtype)
-
-    # ---- logits, draft distribution, draft tokens, uniforms
-    draft_std = float(s.get("draft_std", 3.0))
-    sigma = float(s.get("sigma", 1.0))
-    tokens = np.zeros((B, T_max), dtype=np.int32)
+        inst.q = np.empty((B, T_max, Hq, D), dtype=store)
+        inst.k_new = np.empty((B, T_max, Hkv, D), dtype=store)
+        inst.v_new = np.empty((B, T_max, Hkv, D), dtype=store)
+        inst.k_cache = np.empty((B, Hkv, L_max, D), dtype=store)
+        inst.v_cache = np.empty((B, Hkv, L_max, D), dtype=store)
     if with_accept:
         inst.target_logits = np.empty((B, T_max, V),
                                       dtype=np.uint16 if logit_dtype == "bf16" else np.float32)
         inst.q_probs = np.empty((B, T_max, V), dtype=np.float32)
-    if not with_accept:
-        # no logits: draft tokens are uniform (only the tree shape matters)
-        for b in range(B):
-            tokens[b, :int(num_nodes[b])] = r_draft.integers(0, V, size=int(num_nodes[b]))
-    for b in (range(B) if with_accept else []):
-        zq = r_logits.standard_normal(size=(T_max, V), dtype=np.float32) * np.float32(draft_std)
-        noise = r_logits.standard_normal(size=(T_max, V), dtype=np.float32) * np.float32(sigma)
-        zp = zq + noise
-        del noise
+    tokens = np.zeros((B, T_max), dtype=np.int32)
+    draft_std = float(s.get("draft_std", 3.0))
+    sigma = float(s.get("sigma", 1.0))
+
+    def one_sequence(b):
+        # ---- attention inputs
+        if with_attn:
+            inst.q[b] = _normal(r_qkv[b], (T_max, Hq, D), 1.0, dtype)
+            inst.k_new[b] = _normal(r_qkv[b], (T_max, Hkv, D), 1.0, dtype)
+            inst.v_new[b] = _normal(r_qkv[b], (T_max, Hkv, D), 1.0, dtype)
+            inst.k_cache[b] = _normal(r_cache[b], (Hkv, L_max, D), 1.0, dtype)
+            inst.v_cache[b] = _normal(r_cache[b], (Hkv, L_max, D), 1.0, dtype)
+        Tb = int(num_nodes[b])
+        rd = r_draft[b]
+        if not with_accept:
+            # no logits: draft tokens are uniform (only the tree shape matters)
+            tokens[b, :Tb] = rd.integers(0, V, size=Tb)
+            return
+        # ---- logits, draft distribution, draft tokens
+        rl = r_logits[b]
+        zq = rl.standard_normal(size=(T_max, V), dtype=np.float32) * np.float32(draft_std)
+        zp = zq + rl.standard_normal(size=(T_max, V), dtype=np.float32) * np.float32(sigma)
         tau = float(taus[b])
         t_eff = tau if tau > 0 else 1.0
         z64 = zq.astype(np.float64) / t_eff
@@ -225,19 +246,20 @@ def make_instance(spec, seed=0, with_attn=True, with_accept=True):
         del z64
         inst.target_logits[b] = bf16_bits_from_f32(zp) if logit_dtype == "bf16" else zp
         inst.q_probs[b] = q32
-        # draft tokens
-        Tb = int(num_nodes[b])
-        tokens[b, 0] = int(r_draft.integers(0, V))
+        tokens[b, 0] = int(rd.integers(0, V))
         par = parent[b, :Tb]
         for n in range(Tb):
             kids = np.nonzero(par == n)[0]
             if kids.size == 0:
                 continue
             if tau > 0:
-                drawn = _draw_children(q32[n].astype(np.float64), kids.size, mode, r_draft)
+                drawn = _draw_children(q32[n].astype(np.float64), kids.size, mode, rd)
             else:
                 drawn = [int(i) for i in np.argsort(-zq[n], kind="stable")[:kids.size]]
             tokens[b, kids] = drawn
+
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(one_sequence, range(B)))
     inst.tokens = tokens
     inst.u_accept = r_unif.random(size=(B, T_max), dtype=np.float32)
     inst.u_sample = r_unif.random(size=(B, T_max), dtype=np.float32)
