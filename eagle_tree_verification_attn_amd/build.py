@@ -27,9 +27,14 @@ CFLAGS = [
 ]
 
 
+# Per-file flags.  attn.hip: scores are finite or -inf (masked), never NaN by
+# construction of the kernel, so max needs no NaN canonicalisation.
+FILE_FLAGS = {"attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (r.stdout + r.stderr).splitlines()
             if "packed-fp32-ops" not in l and l.strip()]

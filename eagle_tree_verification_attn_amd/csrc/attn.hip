@@ -67,15 +67,22 @@ __device__ inline int logical_block(int remap) {
   return (i & 7) * per + (i >> 3);
 }
 
-__device__ inline float wave_max16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Max / sum over the 4 lanes holding one tile column (lanes c, c+16, c+32,
+// c+48), with the gfx950 row-swap permutes: permlane16_swap exchanges the odd
+// 16-lane rows of one operand with the even rows of the other, permlane32_swap
+// the upper half with the lower half; with both operands = v the two results
+// hold the partner values.
+__device__ inline float col_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ inline float wave_sum16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+__device__ inline float col_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -314,22 +321,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
 
-    // ---- online softmax (exp2, scale folded), P packed to bf16 for the PV MFMA
-    bf16x8 pk[NT];
+    // ---- online softmax (exp2, scale folded), P packed to bf16 for the PV MFMA.
+    // The block maxima of all tiles are formed first, without branches; one
+    // wave-uniform branch then raises the running maxima (rare once the first
+    // blocks are seen).
+    float mx[NT];
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
-      float mx = fmaxf(fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3])),
-                       fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3])));
-      mx = wave_max16_32(mx) * p.scale_log2;
-      const bool need = mx > m_run[qt] + 8.0f;
-      if (__any(need)) {
-        const float mnew = need ? mx : m_run[qt];
-        const float alpha = m_run[qt] == -INFINITY ? 0.f : exp2f(m_run[qt] - mnew);
+      const float a0 = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
+      const float a1 = fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]));
+      mx[qt] = fmaxf(a0, a1);
+    }
+    bool need_any = false;
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
+      mx[qt] = col_max4(mx[qt]) * p.scale_log2;
+      need_any |= mx[qt] > m_run[qt] + 8.0f;
+    }
+    if (__any(need_any)) {
+#pragma unroll
+      for (int qt = 0; qt < NT; ++qt) {
+        const bool need = mx[qt] > m_run[qt] + 8.0f;
+        const float mnew = need ? mx[qt] : m_run[qt];
+        const float alpha = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - mnew);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
         l_part[qt] *= alpha;
         m_run[qt] = mnew;
       }
+    }
+    bf16x8 pk[NT];
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) {
       const float mu = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
       float pv[8];
 #pragma unroll
@@ -364,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // ---- epilogue
 #pragma unroll
   for (int qt = 0; qt < NT; ++qt) {
-    const float l = wave_sum16_32(l_part[qt]);
+    const float l = col_sum4(l_part[qt]);
     const int r = rrow[qt];
     if (r >= p.T_max * G) continue;
     const int t = r / G, h = kvh * G + r % G;
@@ -536,6 +559,20 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
 // ----------------------------------------------------------------------------
 // host side: launch planning
 // ----------------------------------------------------------------------------
+const void* variant_kernel(int D, int nt, int nw) {
+  switch (D * 100 + nt * 10 + nw) {
+    case 12834: return (const void*)k_attn_bf16<128, 3, 4>;
+    case 12824: return (const void*)k_attn_bf16<128, 2, 4>;
+    case 12821: return (const void*)k_attn_bf16<128, 2, 1>;
+    case 12811: return (const void*)k_attn_bf16<128, 1, 1>;
+    case 6444: return (const void*)k_attn_bf16<64, 4, 4>;
+    case 6434: return (const void*)k_attn_bf16<64, 3, 4>;
+    case 6421: return (const void*)k_attn_bf16<64, 2, 1>;
+    case 6411: return (const void*)k_attn_bf16<64, 1, 1>;
+    default: return nullptr;
+  }
+}
+
 namespace {
 struct Variant {
   int D, nt, nw;
@@ -548,7 +585,7 @@ const Variant kVariants[] = {
     {64, 4, 4, 1.0f},  {64, 3, 4, 1.0f},  {64, 2, 1, 1.0f},  {64, 1, 1, 1.0f},
 };
 // One more pass over the keys of a (sequence, KV head), in padded-row units.
-constexpr float kRereadRows = 160.f;
+constexpr float kRereadRows = 60.f;
 
 size_t smem_bytes(int D, int T_max) {
   const int W = (T_max + 63) / 64;
@@ -556,6 +593,27 @@ size_t smem_bytes(int D, int T_max) {
   return 2 * stage * sizeof(uint16_t) + (size_t)T_max * W * sizeof(uint64_t);
 }
 }  // namespace
+
+// Workgroups of one MFMA variant resident per CU (occupancy query, cached per
+// device and variant; 2 when the runtime cannot tell).
+int resident_groups(int D, int nt, int nw, size_t smem) {
+  static int cache[64][16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int idx = -1, i = 0;
+  for (const Variant& v : kVariants) {
+    if (v.D == D && v.nt == nt && v.nw == nw) idx = i;
+    ++i;
+  }
+  if (idx < 0) return 2;
+  if (cache[dev][idx] == 0) {
+    const void* fn = variant_kernel(D, nt, nw);
+    int n = 0;
+    if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, nw * 64, smem) != hipSuccess || n < 1) n = 2;
+    cache[dev][idx] = n;
+  }
+  return cache[dev][idx];
+}
 
 bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* pl) {
   const DeviceInfo& di = device_info();
@@ -604,10 +662,21 @@ bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* pl) {
         }
       }
     }
-    long groups = units * pl->msplit;
-    long ls = 1;
-    while (groups * ls < 2L * di.num_cu && keys / (ls * 2) >= 8L * BK) ls *= 2;
-    pl->lsplit = (int)ls;
+    // Key splits.  With k workgroups landing on a CU, each doing 1/ls of a
+    // unit's keys, the CU is busy ~ k/ls / thr(k), where two or more
+    // workgroups sharing a CU run 1.6x the throughput of one alone; each
+    // extra split costs a little (partials written and merged).
+    const long groups = units * pl->msplit;
+    float best = -1.f;
+    for (long ls = 1; ls <= 16; ++ls) {
+      if (ls > 1 && keys / ls < 4L * BK) break;
+      const long k = (groups * ls + di.num_cu - 1) / di.num_cu;
+      const float cost = (float)k / (float)ls / (k >= 2 ? 1.6f : 1.f) + 0.02f * (float)(ls - 1);
+      if (best < 0.f || cost < best - 1e-6f) {
+        best = cost;
+        pl->lsplit = (int)ls;
+      }
+    }
   }
   // tuning override: SV_ATTN_LSPLIT=n forces n key ranges per row
   if (const char* ov = getenv("SV_ATTN_LSPLIT")) {
@@ -616,6 +685,10 @@ bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* pl) {
   }
   const long per = (keys + pl->lsplit - 1) / pl->lsplit;
   pl->chunk = (int)((per + 63) / 64 * 64);
+  if (getenv("SV_DEBUG_PLAN"))
+    fprintf(stderr, "sv attention plan: kernel=%d nt=%d nwave=%d rows/wg=%d msplit=%d lsplit=%d chunk=%d cus=%d resident=%d\n",
+            pl->kernel, pl->nt, pl->nwave, pl->rows_per_wg, pl->msplit, pl->lsplit, pl->chunk, di.num_cu,
+            pl->kernel == 0 ? resident_groups(a->D, pl->nt, pl->nwave, smem_bytes(a->D, t->T_max)) : 0);
   pl->ws_bytes = 0;
   if (pl->lsplit > 1) {
     const size_t rows = (size_t)t->B * t->T_max * a->Hq * pl->lsplit;
