@@ -92,115 +92,159 @@ __device__ inline bool greedy_temp(float tau) { return !(tau > 0.f); }
 // ----------------------------------------------------------------------------
 // k_vocab_stats
 // ----------------------------------------------------------------------------
-// Loads up to 8 consecutive logits of one row as floats (vector path when the
-// 8 are aligned and inside the chunk).
-template <bool VEC>
-__device__ inline void load8(const void* row, int bf16, int i0, int iend, float x[8]) {
-  if (VEC && bf16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(row) + i0);
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-  } else if (VEC) {
-    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(row) + i0);
-    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(row) + i0 + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  } else {
+// Per-thread batches of kStatsBatch groups of 8 logits are loaded (as raw
+// 16-byte words) before any arithmetic, so each thread keeps kStatsBatch (bf16)
+// or 2 * kStatsBatch (fp32) 16-byte loads in flight.
+constexpr int kStatsBatch = 8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool BF16, int H>
+__device__ inline float elem8(const u32x4 (&w)[H], int e) {
+  if (BF16) {
+    const uint32_t x = w[0][e >> 1];
+    return (e & 1) ? bf16_hi(x) : bf16_lo(x);
+  }
+  return __uint_as_float(w[e >> 2][e & 3]);
+}
+
+// Loads one item's share for this thread: kStatsBatch groups of 8 logits at
+// vocabulary index base + q * threads * 8 (addresses clamped into the chunk so
+// every load is unconditional).
+template <bool BF16, bool VEC, int RH = BF16 ? 1 : 2>
+__device__ inline void stats_load(const void* logits, size_t row, int V, int base, int i0, int i1,
+                                  u32x4 (&raw)[kStatsBatch][RH]) {
+  const uint16_t* rowh = reinterpret_cast<const uint16_t*>(logits) + row * V;
+  const float* rowf = reinterpret_cast<const float*>(logits) + row * V;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (i0 + e < iend) ? load_logit(row, (size_t)(i0 + e), bf16) : -INFINITY;
+  for (int q = 0; q < kStatsBatch; ++q) {
+    const int i = base + q * kAccThreads * 8;
+    const int ic = i < i1 ? i : i0;
+    if (VEC) {
+      if (BF16) {
+        raw[q][0] = *reinterpret_cast<const u32x4*>(rowh + ic);
+      } else {
+        raw[q][0] = *reinterpret_cast<const u32x4*>(rowf + ic);
+        raw[q][RH - 1] = *reinterpret_cast<const u32x4*>(rowf + ic + 4);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int v = (ic + e < i1) ? ic + e : i0;
+        if (BF16) {
+          const uint32_t h = rowh[v];
+          raw[q][0][e >> 1] = (e & 1) ? (raw[q][0][e >> 1] | (h << 16)) : h;
+        } else {
+          raw[q][(e >> 2) % RH][e & 3] = __float_as_uint(rowf[v]);
+        }
+      }
+    }
   }
 }
 
-template <bool VEC>
+// One workgroup per item (row b * T_max + n, vocabulary chunk c); each thread
+// issues its whole batch of loads before any arithmetic.
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kAccThreads) void k_vocab_stats(StatsParams p) {
   __shared__ float red_m[kAccThreads / 64], red_s[kAccThreads / 64];
   __shared__ int red_i[kAccThreads / 64], red_f[kAccThreads / 64];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int cidx = blockIdx.x;
-  const int row = blockIdx.y;            // b * T_max + n
-  const int b = row / p.T_max;
-  const int n = row % p.T_max;
+  const long row = blockIdx.y;            // b * T_max + n
+  const int b = (int)(row / p.T_max);
+  const int n = (int)(row % p.T_max);
   if (cidx == 0 && row == 0)
     for (int i = tid; i < p.ngroups; i += kAccThreads) p.sync[i] = 0;
   const int Tb = p.num_nodes[b];
   if (p.status[b] != SV_TREE_OK || n >= Tb || Tb > p.T_max) return;
-  const float tau = p.temperature[b];
-  const bool greedy = greedy_temp(tau);
-  const int i0 = cidx * p.chunk;
-  const int i1 = min(i0 + p.chunk, p.V);
-  const void* rowp = p.bf16 ? (const void*)(reinterpret_cast<const uint16_t*>(p.logits) + (size_t)row * p.V)
-                            : (const void*)(reinterpret_cast<const float*>(p.logits) + (size_t)row * p.V);
-  bool bad = false;
-  float m = -INFINITY;
-  int am = 0x7FFFFFFF;
-  float s = 0.f;
-  if (greedy) {
-    for (int i = i0 + tid * 8; i < i1; i += kAccThreads * 8) {
-      float x[8];
-      load8<VEC>(rowp, p.bf16, i, i1, x);
+  constexpr int RH = BF16 ? 1 : 2;   // 16-byte words per group of 8 logits
+  u32x4 raw[kStatsBatch][RH];
+  const int i0 = cidx * p.chunk, i1 = min(i0 + p.chunk, p.V);
+  {
+    const float tau = p.temperature[b];
+    const bool greedy = greedy_temp(tau);
+    const float k = greedy ? 0.f : kLog2e / tau;
+    uint32_t badbits = 0u;
+    float m = -INFINITY, s = 0.f;
+    int am = 0x7FFFFFFF;
+    const int base = i0 + tid * 8;
+    // chunks hold at most threads * 8 * kStatsBatch entries (host-side plan)
+    stats_load<BF16, VEC>(p.logits, (size_t)row, p.V, base, i0, i1, raw);
+    // Non-finite test on the raw words: an all-ones exponent field plus one
+    // carries into the field's top bit.  Clamped loads repeat real entries of
+    // this chunk, so they change neither this flag nor the maximum.
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (i + e < i1) bad |= !isfinite(x[e]);
-        if (x[e] > m) { m = x[e]; am = i + e; }   // strict: keeps the lowest index per thread
-      }
-    }
-  } else {
-    const float k = kLog2e / tau;
-    // first the thread's max, then its sum at that max (online across strides)
-    for (int i = i0 + tid * 8; i < i1; i += kAccThreads * 8) {
-      float x[8];
-      load8<VEC>(rowp, p.bf16, i, i1, x);
-      float bm = -INFINITY;
+    for (int q = 0; q < kStatsBatch; ++q) {
+      if (BF16) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (i + e < i1) bad |= !isfinite(x[e]);
-        bm = fmaxf(bm, x[e]);
-      }
-      if (bm > m) {
-        s = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - bm) * k);
-        m = bm;
-      }
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f((x[e] - m) * k);
-      }
-    }
-  }
-  // workgroup reduction: (max, argmax-lowest) or (max, sum), flags
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int off = 32; off > 0; off >>= 1) {
-    const float om = __shfl_xor(m, off);
-    const int oi = __shfl_xor(am, off);
-    const float os = __shfl_xor(s, off);
-    if (greedy) {
-      if (om > m || (om == m && oi < am)) { m = om; am = oi; }
-    } else {
-      const float nm = fmaxf(m, om);
-      const float a = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - nm) * (kLog2e / tau));
-      const float c = (om == -INFINITY) ? 0.f : os * __builtin_amdgcn_exp2f((om - nm) * (kLog2e / tau));
-      s = a + c;
-      m = nm;
-    }
-  }
-  const bool any_bad = __any(bad);
-  if (lane == 0) { red_m[wv] = m; red_s[wv] = s; red_i[wv] = am; red_f[wv] = any_bad; }
-  __syncthreads();
-  if (tid == 0) {
-    float M = red_m[0], S = red_s[0];
-    int I = red_i[0], F = red_f[0];
-    for (int w = 1; w < kAccThreads / 64; ++w) {
-      F |= red_f[w];
-      if (greedy) {
-        if (red_m[w] > M || (red_m[w] == M && red_i[w] < I)) { M = red_m[w]; I = red_i[w]; }
+        for (int j = 0; j < 4; ++j) badbits |= ((raw[q][0][j] & 0x7F807F80u) + 0x00800080u) & 0x80008000u;
       } else {
-        const float nm = fmaxf(M, red_m[w]);
-        const float a = (M == -INFINITY) ? 0.f : S * __builtin_amdgcn_exp2f((M - nm) * (kLog2e / tau));
-        const float c = (red_m[w] == -INFINITY) ? 0.f : red_s[w] * __builtin_amdgcn_exp2f((red_m[w] - nm) * (kLog2e / tau));
-        S = a + c;
-        M = nm;
+#pragma unroll
+        for (int h = 0; h < RH; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) badbits |= ((raw[q][h][j] & 0x7F800000u) + 0x00800000u) & 0x80000000u;
       }
     }
-    if (F) { M = 0.f; S = 0.f; I = 0; }
-    p.stats[(size_t)row * p.nchunk + cidx] = make_float4(M, S, __int_as_float(I), __int_as_float(F));
+    if (greedy) {
+#pragma unroll
+      for (int q = 0; q < kStatsBatch; ++q) {
+        const int i = base + q * kAccThreads * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = elem8<BF16, RH>(raw[q], e);
+          if (i + e < i1 && x > m) { m = x; am = i + e; }   // strict: lowest index per thread
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kStatsBatch; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, elem8<BF16, RH>(raw[q], e));
+      const float mk = m * k;
+#pragma unroll
+      for (int q = 0; q < kStatsBatch; ++q) {
+        const int i = base + q * kAccThreads * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          s += (i + e < i1) ? __builtin_amdgcn_exp2f(fmaf(elem8<BF16, RH>(raw[q], e), k, -mk)) : 0.f;
+      }
+    }
+    // workgroup reduction: (max, argmax-lowest) or (max, sum), flags
+    for (int off = 32; off > 0; off >>= 1) {
+      const float om = __shfl_xor(m, off);
+      const int oi = __shfl_xor(am, off);
+      const float os = __shfl_xor(s, off);
+      if (greedy) {
+        if (om > m || (om == m && oi < am)) { m = om; am = oi; }
+      } else {
+        const float nm = fmaxf(m, om);
+        const float a = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - nm) * k);
+        const float c = (om == -INFINITY) ? 0.f : os * __builtin_amdgcn_exp2f((om - nm) * k);
+        s = a + c;
+        m = nm;
+      }
+    }
+    const bool any_bad = __any(badbits != 0u);
+    if (lane == 0) { red_m[wv] = m; red_s[wv] = s; red_i[wv] = am; red_f[wv] = any_bad; }
+    __syncthreads();
+    if (tid == 0) {
+      float M = red_m[0], S = red_s[0];
+      int I = red_i[0], F = red_f[0];
+      for (int w = 1; w < kAccThreads / 64; ++w) {
+        F |= red_f[w];
+        if (greedy) {
+          if (red_m[w] > M || (red_m[w] == M && red_i[w] < I)) { M = red_m[w]; I = red_i[w]; }
+        } else {
+          const float nm = fmaxf(M, red_m[w]);
+          const float a = (M == -INFINITY) ? 0.f : S * __builtin_amdgcn_exp2f((M - nm) * k);
+          const float c = (red_m[w] == -INFINITY) ? 0.f : red_s[w] * __builtin_amdgcn_exp2f((red_m[w] - nm) * k);
+          S = a + c;
+          M = nm;
+        }
+      }
+      if (F) { M = 0.f; S = 0.f; I = 0; }
+      p.stats[(size_t)row * p.nchunk + cidx] = make_float4(M, S, __int_as_float(I), __int_as_float(F));
+    }
   }
 }
 
@@ -316,13 +360,23 @@ struct GroupSync {
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
+  // Per-sequence data gathered once into LDS, so the walk's scalar decisions
+  // read LDS instead of chaining dependent global loads.
   __shared__ int par_s[kMaxT];
   __shared__ int tok_s[kMaxT];
   __shared__ int path_s[kMaxT];
+  __shared__ float m_s[kMaxT];    // row max of the target logits
+  __shared__ float ls_s[kMaxT];   // log2 of sum exp((z - m) / tau) (stochastic rows)
+  __shared__ int am_s[kMaxT];     // lowest-index argmax (greedy rows)
+  __shared__ float zx_s[kMaxT];   // logit of node c's token in its parent's row
+  __shared__ float qx_s[kMaxT];   // q of node c's token in its parent's row
+  __shared__ float ua_s[kMaxT];
+  __shared__ float us_s[kMaxT];
   __shared__ float red[kAccThreads / 64];
   __shared__ float masses[64];
   __shared__ float bcast;
   __shared__ int ibcast;
+  __shared__ int flags_s;
 
   const int tid = threadIdx.x;
   const int grp = blockIdx.x / p.nchunk;
@@ -342,24 +396,56 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
     if (st == SV_TREE_OK && (Tb < 1 || Tb > p.T_max)) st = SV_TREE_E_COUNT;
     const float tau = p.temperature[b];
     const bool greedy = greedy_temp(tau);
+    const float k = greedy ? 0.f : kLog2e / tau;
     int32_t* onodes = p.out_nodes + (size_t)b * p.T_max;
     int32_t* otoks = p.out_tokens + (size_t)b * p.T_max;
+    const size_t rowbase = (size_t)b * p.T_max;
+    __syncthreads();
+    if (tid == 0) flags_s = 0;
     __syncthreads();
     if (st == SV_TREE_OK) {
+      // round 1: tree, tokens, uniforms, per-row statistics
       for (int i = tid; i < Tb; i += kAccThreads) {
-        par_s[i] = p.parent[(size_t)b * p.T_max + i];
-        tok_s[i] = p.tokens[(size_t)b * p.T_max + i];
+        par_s[i] = p.parent[rowbase + i];
+        const int x = p.tokens[rowbase + i];
+        tok_s[i] = x;
+        ua_s[i] = p.u_accept[rowbase + i];
+        us_s[i] = p.u_sample[rowbase + i];
+        int f = (x < 0 || x >= p.V) ? 1 : 0;
+        const float4* srow = p.stats + (rowbase + i) * p.nchunk;
+        float m = -INFINITY, ssum = 0.f;
+        int am = 0;
+        for (int cc = 0; cc < p.nchunk; ++cc) {
+          const float4 v = srow[cc];
+          f |= __float_as_int(v.w) != 0 ? 2 : 0;
+          if (v.x > m) { m = v.x; am = __float_as_int(v.z); }   // first chunk with the max: lowest index
+        }
+        if (!greedy)
+          for (int cc = 0; cc < p.nchunk; ++cc) {
+            const float4 v = srow[cc];
+            ssum += v.y * __builtin_amdgcn_exp2f((v.x - m) * k);
+          }
+        m_s[i] = m;
+        am_s[i] = am;
+        ls_s[i] = greedy ? 0.f : __log2f(ssum);
+        if (f) atomicOr(&flags_s, f);
       }
       __syncthreads();
-      int badtok = 0, badrow = 0;
-      for (int i = tid; i < Tb; i += kAccThreads) badtok |= (tok_s[i] < 0 || tok_s[i] >= p.V);
-      for (int i = tid; i < Tb * p.nchunk; i += kAccThreads)
-        badrow |= __float_as_int(p.stats[(size_t)b * p.T_max * p.nchunk + i].w) != 0;
-      badtok = __syncthreads_or(badtok);
-      badrow = __syncthreads_or(badrow);
-      if (badtok) st = SV_TREE_E_TOKEN;
-      else if (badrow) st = SV_TREE_E_NONFINITE;
+      const int f = flags_s;
+      if (f & 1) st = SV_TREE_E_TOKEN;
+      else if (f & 2) st = SV_TREE_E_NONFINITE;
       else if (!greedy && p.q_probs == nullptr) st = SV_TREE_E_NOQ;
+      // round 2: each candidate's logit and draft probability in its parent's row
+      if (st == SV_TREE_OK && !greedy) {
+        for (int c = 1 + tid; c < Tb; c += kAccThreads) {
+          const int n = par_s[c], x = tok_s[c];
+          zx_s[c] = load_logit(BF16 ? (const void*)(reinterpret_cast<const uint16_t*>(p.logits) + (rowbase + n) * p.V)
+                                    : (const void*)(reinterpret_cast<const float*>(p.logits) + (rowbase + n) * p.V),
+                               (size_t)x, BF16);
+          qx_s[c] = p.q_probs[(rowbase + n) * p.V + x];
+        }
+      }
+      __syncthreads();
     }
     if (st != SV_TREE_OK) {
       if (w == 0) {
@@ -374,20 +460,12 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
     }
     if (greedy && w != 0) continue;
 
-    const size_t rowbase = (size_t)b * p.T_max;
     int n = 0, path_len = 0, passes = 0, emitted = -1, owner = -1;
     bool sync_ok = true;
     while (true) {
-      // combine the chunk statistics of row n
-      const float4* srow = p.stats + (rowbase + n) * p.nchunk;
-      float m = -INFINITY;
-      int am = 0;
-      for (int cc = 0; cc < p.nchunk; ++cc) {
-        const float4 v = srow[cc];
-        if (v.x > m) { m = v.x; am = __float_as_int(v.z); }   // first chunk with the max: lowest index
-      }
       int acc = -1;
       if (greedy) {
+        const int am = am_s[n];
         for (int i = n + 1; i < Tb; ++i)
           if (par_s[i] == n && tok_s[i] == am) { acc = i; break; }
         if (acc >= 0) {
@@ -400,35 +478,27 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
         owner = 0;
         break;
       }
-      const float k = kLog2e / tau;
-      float s = 0.f;
-      for (int cc = 0; cc < p.nchunk; ++cc) {
-        const float4 v = srow[cc];
-        s += v.y * __builtin_amdgcn_exp2f((v.x - m) * k);
-      }
-      const float ls = __log2f(s);
+      const float m = m_s[n], ls = ls_s[n];
       const void* zrow = BF16 ? (const void*)(reinterpret_cast<const uint16_t*>(p.logits) + (rowbase + n) * p.V)
                               : (const void*)(reinterpret_cast<const float*>(p.logits) + (rowbase + n) * p.V);
       const float* qrow = p.q_probs + (rowbase + n) * p.V;
       // draw masses of P = p_n, from the chunk statistics
       __syncthreads();
       if (tid < p.nchunk) {
-        const float4 v = srow[tid];
+        const float4 v = p.stats[(rowbase + n) * p.nchunk + tid];
         masses[tid] = v.y * __builtin_amdgcn_exp2f((v.x - m) * k - ls);
       }
       float A = 0.f, Wn = 1.f, rm = 0.f, Adraw = 0.f;
       bool loaded = false;
       for (int c = n + 1; c < Tb; ++c) {
         if (par_s[c] != n) continue;
-        const int x = tok_s[c];
-        const float zx = load_logit(zrow, (size_t)x, BF16);
-        const float qx = qrow[x];
-        const float px = __builtin_amdgcn_exp2f(fmaf(zx - m, k, -ls));
+        const float qx = qx_s[c];
+        const float px = __builtin_amdgcn_exp2f(fmaf(zx_s[c] - m, k, -ls));
         const float Px = fmaxf(px - A * qx, 0.f) / Wn;
         const float ci = wor ? 1.f / (1.f - rm) : 1.f;
         const float qix = qx * ci;
         const float ratio = qix > 0.f ? Px / qix : (Px > 0.f ? INFINITY : 0.f);
-        if (p.u_accept[rowbase + c] < ratio) {
+        if (ua_s[c] < ratio) {
           acc = c;
           break;
         }
@@ -489,7 +559,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       __syncthreads();
       float total = 0.f;
       for (int cc = 0; cc < p.nchunk; ++cc) total += masses[cc];
-      const float target = p.u_sample[rowbase + n] * total;
+      const float target = us_s[n] * total;
       float cum = 0.f;
       owner = -1;
       int last_pos = -1;
@@ -630,8 +700,13 @@ sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_
   const bool vec = (a->V % 8) == 0 &&
                    (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0;
   dim3 grid(pl.nchunk, t->B * t->T_max);
-  if (vec) hipLaunchKernelGGL(k_vocab_stats<true>, grid, dim3(kAccThreads), 0, s, sp);
-  else hipLaunchKernelGGL(k_vocab_stats<false>, grid, dim3(kAccThreads), 0, s, sp);
+  if (sp.bf16) {
+    if (vec) hipLaunchKernelGGL((k_vocab_stats<true, true>), grid, dim3(kAccThreads), 0, s, sp);
+    else hipLaunchKernelGGL((k_vocab_stats<true, false>), grid, dim3(kAccThreads), 0, s, sp);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_vocab_stats<false, true>), grid, dim3(kAccThreads), 0, s, sp);
+    else hipLaunchKernelGGL((k_vocab_stats<false, false>), grid, dim3(kAccThreads), 0, s, sp);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("vocab stats launch: %s", hipGetErrorString(e));
