@@ -14,6 +14,10 @@ timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
     python bench.py --kernels-only   (for rocprofv3 runs: kernels + a copy of known size)
+    python bench.py --summarize-counters FETCH.csv WRITE.csv
+        (turns two rocprofv3 --pmc runs of --kernels-only, FETCH_SIZE then
+         WRITE_SIZE, into the per-launch HBM traffic summary of the attention
+         kernel, calibrated against the 1 GiB copy)
 """
 import argparse
 import hashlib
@@ -30,6 +34,9 @@ WORKLOAD = "tree64_llama70b_b32"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 COUNTERS = os.path.join(ROOT, "profiles", "tree_attn_tree64_llama70b_b32_counters.json")
+COPY_BYTES = 1 << 30            # the calibration copy of --kernels-only (read once, written once)
+ATTN_KERNEL = "k_attn_bf16"
+COPY_KERNEL = "neg_kernel"
 ATTN_SRC = os.path.join(ROOT, "eagle_tree_verification_attn_amd", "csrc", "attn.hip")
 
 
@@ -89,6 +96,54 @@ def counters_traffic():
         return None
 
 
+def summarize_counters(fetch_csv, write_csv):
+    """Per-launch HBM bytes of the attention kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by the ratio
+    of the calibration copy's known size to what the same counter read for it."""
+    import csv
+    import statistics
+
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        attn = [v for (d, k), v in vals.items() if ATTN_KERNEL in k]
+        copy = [v for (d, k), v in vals.items() if COPY_KERNEL in k]
+        if not attn or not copy:
+            raise SystemExit(f"{path}: no {ATTN_KERNEL} or {COPY_KERNEL} dispatches with {counter}")
+        return statistics.mean(attn), statistics.mean(copy), len(attn), len(copy)
+
+    fa, fc, na, nc = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wa, wc, _, _ = per_dispatch(write_csv, "WRITE_SIZE")
+    f_factor = (COPY_BYTES / 1024.0) / fc
+    w_factor = (COPY_BYTES / 1024.0) / wc
+    hbm = 1024.0 * (fa * f_factor + wa * w_factor)
+    out = {
+        "kernel": f"{ATTN_KERNEL} (sv_tree_attn), workload {WORKLOAD}",
+        "attn_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch --output-format csv "
+            "-- python3 bench.py --kernels-only",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write --output-format csv "
+            "-- python3 bench.py --kernels-only",
+            "python3 bench.py --summarize-counters gpurun_out/pmc_fetch/fetch_counter_collection.csv "
+            "gpurun_out/pmc_write/write_counter_collection.csv"],
+        "attn_dispatches": na, "copy_dispatches": nc,
+        "attn_fetch_kib_per_launch": round(fa, 1), "attn_write_kib_per_launch": round(wa, 1),
+        "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib_per_launch": round(fc, 1), "copy_write_kib_per_launch": round(wc, 1),
+        "fetch_scale": round(f_factor, 5), "write_scale": round(w_factor, 5),
+        "hbm_bytes_per_launch": round(hbm),
+    }
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(inst, seconds):
     """The oracle on a bounded sample: whole sequences (attention for all heads,
     target softmax and walk), scaled to steps/s of the full batch."""
@@ -128,7 +183,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels-only", action="store_true",
                     help="launch the kernels a few times plus a 1 GiB copy (for rocprofv3)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(sequences shard across GPUs with no communication: run one process per GPU)",
@@ -158,12 +217,12 @@ def main():
             dev.tree_attn()
         for _ in range(5):
             dev.spec_accept()
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)      # calibration: reads and writes COPY_BYTES once
         torch.cuda.synchronize()
-        print("bench: kernels-only done (copy size 1073741824 bytes)", file=sys.stderr, flush=True)
+        print(f"bench: kernels-only done (copy size {COPY_BYTES} bytes)", file=sys.stderr, flush=True)
         return
 
     for _ in range(args.warmup):
