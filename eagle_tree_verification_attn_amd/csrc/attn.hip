@@ -67,7 +67,7 @@ __device__ inline int logical_block(int remap) {
   return (i & 7) * per + (i >> 3);
 }
 
-// Max / sum over the 4 lanes holding one tile column (lanes c, c+16, c+32,
+// Max over the 4 lanes holding one tile column (lanes c, c+16, c+32,
 // c+48), with the gfx950 row-swap permutes: permlane16_swap exchanges the odd
 // 16-lane rows of one operand with the even rows of the other, permlane32_swap
 // the upper half with the lower half; with both operands = v the two results
@@ -77,12 +77,6 @@ __device__ inline float col_max4(float v) {
   v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ inline float col_sum4(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -104,21 +98,57 @@ __device__ inline bf16x4 lds_read_tr16(const __bf16* p) {
       (lds_bf16*)(p)));
 }
 
+// Direct global -> LDS copy, 16 bytes per lane (global_load_lds_dwordx4): lane
+// i of the wave writes LDS bytes [m0 + 16 i, m0 + 16 i + 16).  Issued as
+// inline asm so that the compiler's wait-count bookkeeping (which would wait
+// for every outstanding copy before any LDS read) stays out of the pipeline;
+// the kernel waits for its copies itself with s_waitcnt vmcnt.  m0 is only
+// ever set right here.
+__device__ inline void copy16_to_lds(const void* gptr, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_byte_addr) : "memory");
+}
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order), then join the workgroup barrier.
+template <int N>
+__device__ inline void wait_copies_and_sync() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+__device__ inline uint32_t lds_byte_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
+// K/V tiles are stored unpadded, BK rows of D elements, with the 16-byte
+// segments of row r permuted by XOR with kv_swizzle(r).  With 64 LDS banks of
+// 4 bytes: the 16 rows of a score fragment read (one segment each) and the 8
+// rows x 2 segments of 32 lanes of a transposed V read land in distinct banks.
+template <int D>
+__device__ inline int kv_swizzle(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+
+// Copy-ring depth: key blocks in flight ahead of the one being computed is
+// kStages - 1.
+constexpr int kStages = 4;
+
 template <int D, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_bf16(AttnParams p) {
   constexpr int NTHR = NW * 64;
-  constexpr int KS = D + 8;    // LDS row stride (elements) of the K and V tiles [BK][KS]
-  constexpr int K_ELEMS = BK * KS;
-  constexpr int STAGE = 2 * K_ELEMS;      // K tile then V tile
-  constexpr int KCH = BK * D / 8;         // 16-byte chunks per tile
-  constexpr int KPT = (KCH + NTHR - 1) / NTHR;
-  static_assert(KCH % NTHR == 0 || NTHR > KCH, "chunk split");  // extra threads repeat chunks
+  constexpr int TILE = BK * D;            // elements of one K or V tile
+  constexpr int STAGE = 2 * TILE;         // K tile then V tile
+  constexpr int SEGS = D / 8;             // 16-byte segments per row
+  constexpr int RPI = 64 / SEGS;          // rows one copy instruction fills
+  constexpr int IPT = BK / RPI;           // copy instructions per tile
+  static_assert(IPT % NW == 0, "copy split");
+  constexpr int IPW = IPT / NW;           // per wave and tile
+  constexpr int CPB = 2 * IPW;            // copies per wave and key block (K and V)
   constexpr int DK = D / 32;              // MFMA k-steps over the head dim
   constexpr int DT = D / 16;              // 16-row output tiles over the head dim
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
-  uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem_raw + 2 * STAGE * sizeof(__bf16));
+  uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem_raw + kStages * STAGE * sizeof(__bf16));
 
   const int lb = logical_block(p.remap);
   const int ms_i = lb % p.msplit;
@@ -211,68 +241,106 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   }
 
-  f32x4 acc[NT][DT];
-  float m_run[NT], l_part[NT];
+  // acc: O^T tiles; lsum: the row sums of P, accumulated by an MFMA with an
+  // all-ones A operand, so every element of lsum[qt] holds its column's sum.
+  // m_run is in log2 units; thr is the raw score above which the running max
+  // must be raised (m_run + 8 in raw units), mu the exp2 offset.
+  f32x4 acc[NT][DT], lsum[NT];
+  float m_run[NT], thr[NT], mu[NT];
+  const float inv_scale_log2 = 1.f / p.scale_log2;
 #pragma unroll
   for (int qt = 0; qt < NT; ++qt) {
     m_run[qt] = -INFINITY;
-    l_part[qt] = 0.f;
+    thr[qt] = -INFINITY;
+    mu[qt] = 0.f;
+    lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
-  // ---- staging of one key block: global -> registers -> LDS.  Thread chunk
-  // i covers key (id / (D/8)), dims [8 * (id % (D/8)), +8) of the block, for
-  // K and V alike.  Every load is unconditional and branch-free (so the next
-  // block's loads stay in flight across the whole iteration): each key picks
-  // its source (cache prefix or tree token), and keys past the range end are
-  // clamped to the last valid key (their scores are masked to -inf, so those
-  // rows of V are weighted by exactly 0).
-  u32x4 kst[KPT], vst[KPT];
-  int ckey[KPT], cseg[KPT];
+  // ---- staging: a ring of kStages (K, V) tile pairs in LDS, filled by direct
+  // copies.  Copy instruction j of wave w fills tile rows [(w IPW + j) RPI,
+  // + RPI); lane l of it loads row l / SEGS, segment (l % SEGS) ^ swizzle(row).
+  // Keys past the range end are clamped to the last valid key (their scores
+  // are masked to -inf, so those rows of V are weighted by exactly 0).
+  int drow[IPW];
+  uint32_t dseg[IPW], doff[IPW];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int id = (tid + i * NTHR) % KCH;
-    ckey[i] = id / (D / 8);
-    cseg[i] = id % (D / 8);
+  for (int j = 0; j < IPW; ++j) {
+    drow[j] = (wave * IPW + j) * RPI + lane / SEGS;
+    dseg[j] = (uint32_t)(((lane % SEGS) ^ kv_swizzle<D>(drow[j])) * 8);
+    doff[j] = (uint32_t)(drow[j] * D) + dseg[j];
   }
-  auto load_block = [&](int blk) {
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_byte_address(smem_raw));
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)(wave * IPW * 1024));
+  const int fast_end = min(Lb, kend);   // blocks ending here or before are all cache keys
+  const uint64_t kc_addr = reinterpret_cast<uint64_t>(kc), vc_addr = reinterpret_cast<uint64_t>(vc);
+  const uint64_t kn_addr = reinterpret_cast<uint64_t>(kn), vn_addr = reinterpret_cast<uint64_t>(vn);
+  auto issue_block = [&](int blk, int stage) {
+    const uint32_t kl = lds0 + (uint32_t)(stage * STAGE * 2) + wave_lds;
+    const uint32_t vl = kl + TILE * 2;
+    if (blk + BK <= fast_end) {
+      // whole block inside the cache prefix: one uniform base, fixed lane offsets
+      const __bf16* kb = kc + (size_t)blk * D;
+      const __bf16* vb = vc + (size_t)blk * D;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int jr = blk + ckey[i];
-      const int j = jr < kend ? jr : kend - 1;
-      const bool in_cache = j < Lb;
-      // 32-bit element offset inside the selected source; no branches, so
-      // the loads of one block are issued back to back
-      const uint32_t loc = in_cache ? (uint32_t)j * D : (uint32_t)(j - Lb) * new_stride32;
-      const __bf16* kb = in_cache ? kc : kn;
-      const __bf16* vb = in_cache ? vc : vn;
-      kst[i] = *reinterpret_cast<const u32x4*>(kb + loc + cseg[i] * 8);
-      vst[i] = *reinterpret_cast<const u32x4*>(vb + loc + cseg[i] * 8);
+      for (int j = 0; j < IPW; ++j) {
+        copy16_to_lds(kb + doff[j], kl + j * 1024);
+        copy16_to_lds(vb + doff[j], vl + j * 1024);
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int jr = blk + drow[j];
+      const int jj = jr < kend ? jr : kend - 1;
+      const bool in_cache = jj < Lb;
+      const uint64_t loc = 2ull * ((in_cache ? (uint32_t)jj * D : (uint32_t)(jj - Lb) * new_stride32) + dseg[j]);
+      const uint64_t ka = (in_cache ? kc_addr : kn_addr) + loc;
+      const uint64_t va = (in_cache ? vc_addr : vn_addr) + loc;
+      copy16_to_lds(reinterpret_cast<const void*>(ka), kl + j * 1024);
+      copy16_to_lds(reinterpret_cast<const void*>(va), vl + j * 1024);
     }
   };
-  auto store_block = [&](int buf) {
-    __bf16* ks = smem + buf * STAGE;
-    __bf16* vs = ks + K_ELEMS;
+
+  // LDS element offsets of this lane's fragment reads (swizzled):
+  //   K: row 16 kt + c, segment 4 kk + g        (score MFMA A operand);
+  //   V: row 4 g + c / 4 (+16), dims 16 dt + 4 (c % 4) .. +3 (transposed read).
+  uint32_t koff[DK], voff[DT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int off = ckey[i] * KS + cseg[i] * 8;
-      *reinterpret_cast<u32x4*>(ks + off) = kst[i];
-      *reinterpret_cast<u32x4*>(vs + off) = vst[i];
-    }
-  };
+  for (int kk = 0; kk < DK; ++kk) koff[kk] = (uint32_t)(c * D + (((4 * kk + g) ^ kv_swizzle<D>(c)) * 8));
+  {
+    const int rv = 4 * g + (c >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      voff[dt] = (uint32_t)(rv * D + (((2 * dt + ((c >> 1) & 1)) ^ kv_swizzle<D>(rv)) * 8) + (c & 1) * 4);
+  }
+
+  // The query loads complete here: the empty asm needs the registers, so the
+  // compiler waits for them once, not at their first use inside the loop
+  // (where its wait would also cover the outstanding copies).
+#pragma unroll
+  for (int qt = 0; qt < NT; ++qt)
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) asm volatile("" : "+v"(qreg[qt][kk]));
 
   const int nblk = (kend - kbeg + BK - 1) / BK;
-  load_block(kbeg);
-  store_block(0);
-  __syncthreads();
+  __syncthreads();   // ancestor rows in LDS
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < nblk) issue_block(kbeg + i * BK, i);
 
   for (int it = 0; it < nblk; ++it) {
     const int blk = kbeg + it * BK;
-    const int buf = it & 1;
-    if (it + 1 < nblk) load_block(blk + BK);
-    const __bf16* ks = smem + buf * STAGE;
-    const __bf16* vs = ks + K_ELEMS;
+    // block it has landed (for every wave) and every wave is done with block
+    // it - 1, whose ring slot the next copy refills
+    if (it + kStages - 2 < nblk) wait_copies_and_sync<(kStages - 2) * CPB>();
+    else wait_copies_and_sync<0>();
+    if (it + kStages - 1 < nblk) issue_block(blk + (kStages - 1) * BK, (it + kStages - 1) % kStages);
+    const __bf16* ks = smem + (it % kStages) * STAGE;
+    const __bf16* vs = ks + TILE;
 
     // ---- scores S^T (2 sub-tiles of 16 keys)
     f32x4 s[NT][2];
@@ -280,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int kk = 0; kk < DK; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * kt + c) * KS + 32 * kk + 8 * g);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + 16 * kt * D + koff[kk]);
 #pragma unroll
         for (int qt = 0; qt < NT; ++qt)
           s[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -322,44 +390,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 
     // ---- online softmax (exp2, scale folded), P packed to bf16 for the PV MFMA.
-    // The block maxima of all tiles are formed first, without branches; one
-    // wave-uniform branch then raises the running maxima (rare once the first
-    // blocks are seen).
-    float mx[NT];
+    // Each lane compares its own 8 raw scores per tile with the threshold; only
+    // when some lane exceeds it (rare once the first blocks are seen) does the
+    // wave form the column maxima and raise the running maxima.
+    bool need_any = false;
+    float pm[NT];
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
       const float a0 = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
       const float a1 = fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]));
-      mx[qt] = fmaxf(a0, a1);
-    }
-    bool need_any = false;
-#pragma unroll
-    for (int qt = 0; qt < NT; ++qt) {
-      mx[qt] = col_max4(mx[qt]) * p.scale_log2;
-      need_any |= mx[qt] > m_run[qt] + 8.0f;
+      pm[qt] = fmaxf(a0, a1);
+      need_any |= pm[qt] > thr[qt];
     }
     if (__any(need_any)) {
 #pragma unroll
       for (int qt = 0; qt < NT; ++qt) {
-        const bool need = mx[qt] > m_run[qt] + 8.0f;
-        const float mnew = need ? mx[qt] : m_run[qt];
+        const float mx = col_max4(pm[qt]) * p.scale_log2;
+        const bool need = mx > m_run[qt] + 8.0f;
+        const float mnew = need ? mx : m_run[qt];
         const float alpha = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - mnew);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
-        l_part[qt] *= alpha;
+        lsum[qt] *= alpha;
         m_run[qt] = mnew;
+        mu[qt] = mnew == -INFINITY ? 0.f : mnew;
+        thr[qt] = mnew == -INFINITY ? -INFINITY : (mnew + 8.0f) * inv_scale_log2;
       }
     }
     bf16x8 pk[NT];
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
-      const float mu = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
       float pv[8];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[kt * 4 + i] = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][i], p.scale_log2, -mu));
-      l_part[qt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        for (int i = 0; i < 4; ++i) pv[kt * 4 + i] = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][i], p.scale_log2, -mu[qt]));
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
@@ -369,25 +434,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // ---- O^T += V^T P^T.  Lane (g, c) needs V[key][16 dt + c] for keys
     // 4g + k and 16 + 4g + k (k = 0..3); as a source of the transposed read it
     // addresses row 4g + c/4 (+16), dims 16 dt + 4 (c % 4) .. +3.
-    const __bf16* vsrc = vs + (4 * g + (c >> 2)) * KS + 4 * (c & 3);
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt)
+      lsum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[qt], lsum[qt], 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x4 lo = lds_read_tr16(vsrc + 16 * dt);
-      const bf16x4 hi = lds_read_tr16(vsrc + 16 * KS + 16 * dt);
+      const bf16x4 lo = lds_read_tr16(vs + voff[dt]);
+      const bf16x4 hi = lds_read_tr16(vs + 16 * D + voff[dt]);
       const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int qt = 0; qt < NT; ++qt)
         acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[qt], acc[qt][dt], 0, 0, 0);
     }
-
-    if (it + 1 < nblk) store_block(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue
 #pragma unroll
   for (int qt = 0; qt < NT; ++qt) {
-    const float l = col_sum4(l_part[qt]);
+    const float l = lsum[qt][0];
     const int r = rrow[qt];
     if (r >= p.T_max * G) continue;
     const int t = r / G, h = kvh * G + r % G;
@@ -589,8 +653,8 @@ constexpr float kRereadRows = 60.f;
 
 size_t smem_bytes(int D, int T_max) {
   const int W = (T_max + 63) / 64;
-  const size_t stage = 2 * (size_t)BK * (D + 8);
-  return 2 * stage * sizeof(uint16_t) + (size_t)T_max * W * sizeof(uint64_t);
+  const size_t stage = 2 * (size_t)BK * D;
+  return kStages * stage * sizeof(uint16_t) + (size_t)T_max * W * sizeof(uint64_t);
 }
 }  // namespace
 
