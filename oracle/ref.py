@@ -29,9 +29,10 @@ in the design notes of the repository):
   earlier siblings' tokens removed and renormalised when siblings were drawn
   without replacement, and q itself when drawn i.i.d.;
 * the terminal draw is an inverse CDF in ascending token order;
-* a non-finite target logit in rows 0..T_b-1, a token outside [0, V), or a
-  stochastic sequence without draft probabilities marks the sequence invalid
-  (count 0, outputs -1).
+* a token outside [0, V), a stochastic sequence without draft probabilities,
+  or a non-finite target logit in a row the walk reads (the row of every node
+  it visits) marks the sequence invalid (count 0, outputs -1); rows of nodes
+  the walk never reaches are not inspected.
 
 Parity is pinned by the tests under ``tests/test_oracle_*.py`` (closed forms,
 the worked example trees and numbers the pages print, library routines for the
@@ -235,7 +236,7 @@ def inverse_cdf(P, u):
 #   the correction sampled; this is applied recursively at every node.
 # --------------------------------------------------------------------------
 def accept_walk(parent_row, tokens_row, T_b, zrow, qrow, tau, u_accept_row, u_sample_row,
-                sibling_mode=SIB_WITHOUT_REPLACEMENT):
+                sibling_mode=SIB_WITHOUT_REPLACEMENT, reject_nonfinite=False):
     """Walk one verified tree from the root.
 
     ``zrow(n)`` returns the float64 target logits of node n (the target's
@@ -246,6 +247,10 @@ def accept_walk(parent_row, tokens_row, T_b, zrow, qrow, tau, u_accept_row, u_sa
     passes: one per rejection, one per bonus draw), ``decisions`` (list of
     (kind, node, margin)) and ``exempt_at`` (number of accepted nodes fixed
     before the first decision whose margin is below EXEMPT_MARGIN, or None).
+    With ``reject_nonfinite`` (the input rule of ``spec_accept``), a visited
+    node whose row holds a NaN or an infinity stops the walk, which returns
+    ``{"nonfinite": True, "node": n}`` instead; without it a -inf logit is
+    simply a token of target probability 0.
     """
     children = {n: [] for n in range(T_b)}
     for i in range(1, T_b):
@@ -258,6 +263,8 @@ def accept_walk(parent_row, tokens_row, T_b, zrow, qrow, tau, u_accept_row, u_sa
     while True:
         C = children[n]
         z = zrow(n)
+        if reject_nonfinite and not np.all(np.isfinite(z)):
+            return dict(nonfinite=True, node=n)
         if greedy:
             a = argmax_lowest(z)
             match = [c for c in C if int(tokens_row[c]) == a]
@@ -337,11 +344,6 @@ def spec_accept(parent, num_nodes, tokens, target_logits, logit_dtype, q_probs, 
         if np.any(tk < 0) or np.any(tk >= V):
             status[b] = TREE_E_TOKEN
             continue
-        rows_ok = all(np.all(np.isfinite(to_f64(target_logits[b, n], logit_dtype)))
-                      for n in range(T_b))
-        if not rows_ok:
-            status[b] = TREE_E_NONFINITE
-            continue
         if q_probs is None and float(np.float32(temperature[b])) > 0.0:
             status[b] = TREE_E_NOQ      # stochastic verification needs the draft distribution
             continue
@@ -349,7 +351,11 @@ def spec_accept(parent, num_nodes, tokens, target_logits, logit_dtype, q_probs, 
                         lambda n, b=b: to_f64(target_logits[b, n], logit_dtype),
                         (lambda n, b=b: np.asarray(q_probs[b, n], dtype=np.float64))
                         if q_probs is not None else None,
-                        float(temperature[b]), u_accept[b], u_sample[b], sibling_mode)
+                        float(temperature[b]), u_accept[b], u_sample[b], sibling_mode,
+                        reject_nonfinite=True)
+        if w.get("nonfinite"):
+            status[b] = TREE_E_NONFINITE   # a row the walk read holds a NaN or an infinity
+            continue
         walks[b] = w
         out_nodes[b, :len(w["nodes"])] = w["nodes"]
         out_tokens[b, :w["count"]] = w["emitted"]

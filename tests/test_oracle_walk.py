@@ -297,3 +297,35 @@ def test_one_hot_p_and_q_reduce_to_greedy():
         gre = oracle.accept_walk(parent, tokens, T, lambda n: Zg[n], None, 0.0, np.zeros(T),
                                  np.zeros(T))
         assert sto["nodes"] == gre["nodes"] and sto["emitted"] == gre["emitted"]
+
+
+# ----------------------------------------------------------------------------- input rule
+def _two_child_tree_instance(V=12):
+    """Root with children 1, 2; node 1 has child 3.  q = p at every node, so the
+    walk accepts the first child at each node (special case above) and visits
+    rows 0, 1 and 3, never row 2."""
+    rng = np.random.default_rng(5)
+    parent = np.array([[-1, 0, 0, 1]], dtype=np.int32)
+    z = rng.normal(size=(1, 4, V)).astype(np.float32)
+    q = scipy.special.softmax(z.astype(np.float64), axis=-1).astype(np.float32)
+    tokens = np.array([[0, 3, 4, 5]], dtype=np.int32)
+    return parent, z, q, tokens, rng.random((1, 4)).astype(np.float32), rng.random((1, 4)).astype(np.float32)
+
+
+@pytest.mark.parametrize("row,bad", [(2, np.nan), (2, np.inf), (0, np.nan), (1, -np.inf), (3, np.inf)])
+def test_nonfinite_logits_only_in_rows_the_walk_reads(row, bad):
+    parent, z, q, tokens, ua, us = _two_child_tree_instance()
+    num = np.array([4], dtype=np.int32)
+    clean = oracle.spec_accept(parent, num, tokens, z, "f32", q, np.ones(1, np.float32), ua, us,
+                               np.zeros(1, np.int32), IID)
+    assert clean["out_nodes"][0, :2].tolist() == [1, 3]      # q = p: first children accepted
+    z2 = z.copy()
+    z2[0, row, 7] = bad
+    res = oracle.spec_accept(parent, num, tokens, z2, "f32", q, np.ones(1, np.float32), ua, us,
+                             np.zeros(1, np.int32), IID)
+    if row == 2:   # never visited: the outcome is unchanged
+        assert res["status"][0] == oracle.TREE_OK
+        np.testing.assert_array_equal(res["out_tokens"], clean["out_tokens"])
+    else:
+        assert res["status"][0] == oracle.TREE_E_NONFINITE
+        assert res["out_count"][0] == 0 and (res["out_nodes"] == -1).all()
