@@ -9,19 +9,15 @@
 // the corrected distribution; only when all k are rejected is the correction
 // sampled; the rule is applied recursively at every node of the tree.
 //
-// Two kernels:
-//
-//  k_vocab_stats  one workgroup per (tree position, vocabulary chunk): chunk
-//                 max m_c, sum_c exp((z - m_c) / tau) (stochastic rows) or the
-//                 lowest-index argmax (greedy rows), and a non-finite flag.
-//                 Reads every logits row of the batch once.
-//
-//  k_accept_walk  cooperative launch of groups of `nchunk` workgroups; a group
-//                 walks one sequence at a time, workgroup w owning vocabulary
-//                 chunk w.  All workgroups of a group take the same scalar
-//                 decisions from the same data; each rejection needs the mass
-//                 of the new residual, summed over the vocabulary by all
-//                 workgroups and exchanged through a group barrier.
+// One cooperative kernel, k_accept_walk: groups of `nchunk` workgroups, a
+// group walking one sequence at a time with workgroup w owning vocabulary
+// chunk w.  At each node the walk visits, every workgroup reads its chunk of
+// the node's logits row once into LDS and the group combines the chunk
+// statistics (max, sum exp((z - max) / tau), or the lowest-index argmax for
+// greedy rows, and a non-finite flag) through one barrier; rows of nodes the
+// walk never reaches are not read.  All workgroups take the same scalar
+// decisions from the same exchanged values; each rejection needs the mass of
+// the new residual, summed over the vocabulary and exchanged the same way.
 //
 // Residual bookkeeping.  With p the target distribution of the node, q its
 // draft distribution, and siblings x_1..x_i rejected, the current target is
@@ -44,17 +40,6 @@ constexpr int kAccThreads = 256;
 constexpr int kMaxChunk = 16384;  // vocabulary entries one walk workgroup caches in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct StatsParams {
-  const void* logits;
-  const float* temperature;
-  const int32_t* num_nodes;
-  const int32_t* status;
-  float4* stats;   // [B][T_max][nchunk]: m, s, argmax (int bits), flags (int bits)
-  int* sync;       // [ngroups] group barrier counters, cleared here
-  int B, T_max, V, nchunk, chunk, ngroups;
-  int bf16;
-};
-
 struct WalkParams {
   const int32_t* parent;
   const int32_t* num_nodes;
@@ -69,9 +54,7 @@ struct WalkParams {
   int32_t* out_nodes;
   int32_t* out_count;
   int32_t* out_passes;
-  const float4* stats;
-  int* sync;
-  float* part;     // [ngroups][2][nchunk]
+  uint64_t* xchg;  // [ngroups][2][nchunk][kXWords] exchange words, zeroed by k_accept_clear
   int B, T_max, V, nchunk, chunk, ngroups;
   int bf16, sibling_mode;
 };
@@ -90,12 +73,14 @@ __device__ inline float load_logit(const void* base, size_t idx, int bf16) {
 __device__ inline bool greedy_temp(float tau) { return !(tau > 0.f); }
 
 // ----------------------------------------------------------------------------
-// k_vocab_stats
+// chunk loads
 // ----------------------------------------------------------------------------
-// Per-thread batches of kStatsBatch groups of 8 logits are loaded (as raw
-// 16-byte words) before any arithmetic, so each thread keeps kStatsBatch (bf16)
-// or 2 * kStatsBatch (fp32) 16-byte loads in flight.
-constexpr int kStatsBatch = 8;
+// A workgroup reads its vocabulary chunk of one row with every load issued
+// before any arithmetic: thread t takes kBatch groups of 8 entries at
+// c0 + 8 t + 8 q * threads (q < kBatch); addresses past the chunk end are
+// clamped to the chunk start, so every load is unconditional.
+constexpr int kBatch = 8;
+static_assert(kAccThreads * 8 * kBatch == kMaxChunk, "chunk covered by one batch");
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <bool BF16, int H>
@@ -107,18 +92,17 @@ __device__ inline float elem8(const u32x4 (&w)[H], int e) {
   return __uint_as_float(w[e >> 2][e & 3]);
 }
 
-// Loads one item's share for this thread: kStatsBatch groups of 8 logits at
-// vocabulary index base + q * threads * 8 (addresses clamped into the chunk so
-// every load is unconditional).
+// Raw 16-byte words of the logits: one per group of 8 (bf16) or two (fp32).
+// Without VEC (row not 16-byte aligned or V % 8 != 0) entries are read one by
+// one, entries past the chunk end again clamped.
 template <bool BF16, bool VEC, int RH = BF16 ? 1 : 2>
-__device__ inline void stats_load(const void* logits, size_t row, int V, int base, int i0, int i1,
-                                  u32x4 (&raw)[kStatsBatch][RH]) {
-  const uint16_t* rowh = reinterpret_cast<const uint16_t*>(logits) + row * V;
-  const float* rowf = reinterpret_cast<const float*>(logits) + row * V;
+__device__ inline void load_raw(const void* rowp, int c0, int c1, u32x4 (&raw)[kBatch][RH]) {
+  const uint16_t* rowh = reinterpret_cast<const uint16_t*>(rowp);
+  const float* rowf = reinterpret_cast<const float*>(rowp);
 #pragma unroll
-  for (int q = 0; q < kStatsBatch; ++q) {
-    const int i = base + q * kAccThreads * 8;
-    const int ic = i < i1 ? i : i0;
+  for (int q = 0; q < kBatch; ++q) {
+    const int i = c0 + (threadIdx.x + q * kAccThreads) * 8;
+    const int ic = i < c1 ? i : c0;
     if (VEC) {
       if (BF16) {
         raw[q][0] = *reinterpret_cast<const u32x4*>(rowh + ic);
@@ -129,7 +113,7 @@ __device__ inline void stats_load(const void* logits, size_t row, int V, int bas
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int v = (ic + e < i1) ? ic + e : i0;
+        const int v = (ic + e < c1) ? ic + e : c0;
         if (BF16) {
           const uint32_t h = rowh[v];
           raw[q][0][e >> 1] = (e & 1) ? (raw[q][0][e >> 1] | (h << 16)) : h;
@@ -141,111 +125,146 @@ __device__ inline void stats_load(const void* logits, size_t row, int V, int bas
   }
 }
 
-// One workgroup per item (row b * T_max + n, vocabulary chunk c); each thread
-// issues its whole batch of loads before any arithmetic.
+// Statistics of this workgroup's chunk of one logits row:
+//   stochastic rows: (m_c, s_c) = (chunk max, sum of e(v) = 2^((z(v) - m_c) k)),
+//                    and e(v) stored in LDS at ec[v - c0];
+//   greedy rows:     (m_c, i_c) = (chunk max, its lowest index);
+//   flag: a NaN or an infinity anywhere in the chunk.
+// The result is returned to thread 0 as (m, s or index bits, flag, 0).
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kAccThreads) void k_vocab_stats(StatsParams p) {
-  __shared__ float red_m[kAccThreads / 64], red_s[kAccThreads / 64];
-  __shared__ int red_i[kAccThreads / 64], red_f[kAccThreads / 64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int cidx = blockIdx.x;
-  const long row = blockIdx.y;            // b * T_max + n
-  const int b = (int)(row / p.T_max);
-  const int n = (int)(row % p.T_max);
-  if (cidx == 0 && row == 0)
-    for (int i = tid; i < p.ngroups; i += kAccThreads) p.sync[i] = 0;
-  const int Tb = p.num_nodes[b];
-  if (p.status[b] != SV_TREE_OK || n >= Tb || Tb > p.T_max) return;
-  constexpr int RH = BF16 ? 1 : 2;   // 16-byte words per group of 8 logits
-  u32x4 raw[kStatsBatch][RH];
-  const int i0 = cidx * p.chunk, i1 = min(i0 + p.chunk, p.V);
-  {
-    const float tau = p.temperature[b];
-    const bool greedy = greedy_temp(tau);
-    const float k = greedy ? 0.f : kLog2e / tau;
-    uint32_t badbits = 0u;
-    float m = -INFINITY, s = 0.f;
-    int am = 0x7FFFFFFF;
-    const int base = i0 + tid * 8;
-    // chunks hold at most threads * 8 * kStatsBatch entries (host-side plan)
-    stats_load<BF16, VEC>(p.logits, (size_t)row, p.V, base, i0, i1, raw);
-    // Non-finite test on the raw words: an all-ones exponent field plus one
-    // carries into the field's top bit.  Clamped loads repeat real entries of
-    // this chunk, so they change neither this flag nor the maximum.
+__device__ float4 chunk_stats(const void* rowp, int c0, int c1, bool greedy, float k, float* ec,
+                              float* red_m, float* red_s, int* red_i, int* red_f) {
+  constexpr int RH = BF16 ? 1 : 2;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  u32x4 raw[kBatch][RH];
+  load_raw<BF16, VEC>(rowp, c0, c1, raw);
+  // Non-finite test on the raw words: an all-ones exponent field plus one
+  // carries into the field's top bit.  Clamped loads repeat real entries of
+  // this chunk, so they change neither this flag nor the maximum.
+  uint32_t badbits = 0u;
 #pragma unroll
-    for (int q = 0; q < kStatsBatch; ++q) {
-      if (BF16) {
+  for (int q = 0; q < kBatch; ++q) {
+    if (BF16) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) badbits |= ((raw[q][0][j] & 0x7F807F80u) + 0x00800080u) & 0x80008000u;
-      } else {
-#pragma unroll
-        for (int h = 0; h < RH; ++h)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) badbits |= ((raw[q][h][j] & 0x7F800000u) + 0x00800000u) & 0x80000000u;
-      }
-    }
-    if (greedy) {
-#pragma unroll
-      for (int q = 0; q < kStatsBatch; ++q) {
-        const int i = base + q * kAccThreads * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = elem8<BF16, RH>(raw[q], e);
-          if (i + e < i1 && x > m) { m = x; am = i + e; }   // strict: lowest index per thread
-        }
-      }
+      for (int j = 0; j < 4; ++j) badbits |= ((raw[q][0][j] & 0x7F807F80u) + 0x00800080u) & 0x80008000u;
     } else {
 #pragma unroll
-      for (int q = 0; q < kStatsBatch; ++q)
+      for (int h = 0; h < RH; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, elem8<BF16, RH>(raw[q], e));
-      const float mk = m * k;
+        for (int j = 0; j < 4; ++j) badbits |= ((raw[q][h][j] & 0x7F800000u) + 0x00800000u) & 0x80000000u;
+    }
+  }
+  const bool any_bad = __any(badbits != 0u);
+  float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (greedy) {
+    // (max, lowest index): per thread, per wave, then over the waves
+    float m = -INFINITY;
+    int am = 0x7FFFFFFF;
 #pragma unroll
-      for (int q = 0; q < kStatsBatch; ++q) {
-        const int i = base + q * kAccThreads * 8;
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = c0 + (tid + q * kAccThreads) * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          s += (i + e < i1) ? __builtin_amdgcn_exp2f(fmaf(elem8<BF16, RH>(raw[q], e), k, -mk)) : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const float x = elem8<BF16, RH>(raw[q], e);
+        if (i + e < c1 && x > m) { m = x; am = i + e; }   // strict: lowest index per thread
       }
     }
-    // workgroup reduction: (max, argmax-lowest) or (max, sum), flags
     for (int off = 32; off > 0; off >>= 1) {
       const float om = __shfl_xor(m, off);
       const int oi = __shfl_xor(am, off);
-      const float os = __shfl_xor(s, off);
-      if (greedy) {
-        if (om > m || (om == m && oi < am)) { m = om; am = oi; }
-      } else {
-        const float nm = fmaxf(m, om);
-        const float a = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - nm) * k);
-        const float c = (om == -INFINITY) ? 0.f : os * __builtin_amdgcn_exp2f((om - nm) * k);
-        s = a + c;
-        m = nm;
-      }
+      if (om > m || (om == m && oi < am)) { m = om; am = oi; }
     }
-    const bool any_bad = __any(badbits != 0u);
-    if (lane == 0) { red_m[wv] = m; red_s[wv] = s; red_i[wv] = am; red_f[wv] = any_bad; }
+    __syncthreads();   // the previous user of red_* is done
+    if (lane == 0) { red_m[wv] = m; red_i[wv] = am; red_f[wv] = any_bad; }
     __syncthreads();
     if (tid == 0) {
-      float M = red_m[0], S = red_s[0];
+      float M = red_m[0];
       int I = red_i[0], F = red_f[0];
       for (int w = 1; w < kAccThreads / 64; ++w) {
         F |= red_f[w];
-        if (greedy) {
-          if (red_m[w] > M || (red_m[w] == M && red_i[w] < I)) { M = red_m[w]; I = red_i[w]; }
-        } else {
-          const float nm = fmaxf(M, red_m[w]);
-          const float a = (M == -INFINITY) ? 0.f : S * __builtin_amdgcn_exp2f((M - nm) * k);
-          const float c = (red_m[w] == -INFINITY) ? 0.f : red_s[w] * __builtin_amdgcn_exp2f((red_m[w] - nm) * k);
-          S = a + c;
-          M = nm;
-        }
+        if (red_m[w] > M || (red_m[w] == M && red_i[w] < I)) { M = red_m[w]; I = red_i[w]; }
       }
-      if (F) { M = 0.f; S = 0.f; I = 0; }
-      p.stats[(size_t)row * p.nchunk + cidx] = make_float4(M, S, __int_as_float(I), __int_as_float(F));
+      out = make_float4(M, __int_as_float(I), __int_as_float(F), 0.f);
+    }
+    return out;
+  }
+  // stochastic: the chunk max first, then e(v) and its sum against it (the
+  // clamped entries repeat real ones, so they leave the max unchanged)
+  float m = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, elem8<BF16, RH>(raw[q], e));
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __syncthreads();   // the previous user of red_* is done
+  if (lane == 0) { red_m[wv] = m; red_f[wv] = any_bad; }
+  __syncthreads();
+  float mc = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kAccThreads / 64; ++w) mc = fmaxf(mc, red_m[w]);
+  const float mk = mc * k;
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q) {
+    const int i = c0 + (tid + q * kAccThreads) * 8;
+    float ev[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ev[e] = __builtin_amdgcn_exp2f(fmaf(elem8<BF16, RH>(raw[q], e), k, -mk));
+      s += (i + e < c1) ? ev[e] : 0.f;
+    }
+    if (VEC) {
+      // a clamped group holds entries [c0, c0 + 8) and rewrites them unchanged
+      const int ic = i < c1 ? i : c0;
+      *reinterpret_cast<f32x4*>(ec + (ic - c0)) = f32x4{ev[0], ev[1], ev[2], ev[3]};
+      *reinterpret_cast<f32x4*>(ec + (ic - c0) + 4) = f32x4{ev[4], ev[5], ev[6], ev[7]};
+    } else if (i < c1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (i + e < c1) ec[i - c0 + e] = ev[e];
     }
   }
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) red_s[wv] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float S = 0.f;
+    int F = 0;
+    for (int w = 0; w < kAccThreads / 64; ++w) { S += red_s[w]; F |= red_f[w]; }
+    out = make_float4(mc, S, __int_as_float(F), 0.f);
+  }
+  return out;
+}
+
+// q(v) for v in [c0, c1) of one draft row into qc[v - c0], loads batched.
+template <bool VEC>
+__device__ inline void load_q_chunk(const float* qrow, int c0, int c1, float* qc) {
+  const int tid = threadIdx.x;
+  if (VEC) {
+    u32x4 a[kBatch], b[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = c0 + (tid + q * kAccThreads) * 8;
+      const int ic = i < c1 ? i : c0;
+      a[q] = *reinterpret_cast<const u32x4*>(qrow + ic);
+      b[q] = *reinterpret_cast<const u32x4*>(qrow + ic + 4);
+    }
+    // unconditional stores: a clamped group rewrites entries [0, 8) of the
+    // chunk with the values they already hold
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = c0 + (tid + q * kAccThreads) * 8;
+      const int ic = i < c1 ? i : c0;
+      *reinterpret_cast<u32x4*>(qc + (ic - c0)) = a[q];
+      *reinterpret_cast<u32x4*>(qc + (ic - c0) + 4) = b[q];
+    }
+  } else {
+    for (int i = c0 + tid; i < c1; i += kAccThreads) qc[i - c0] = qrow[i];
+  }
+}
+
+__global__ void k_accept_clear(uint64_t* words, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) words[i] = 0ull;
 }
 
 // ----------------------------------------------------------------------------
@@ -286,78 +305,60 @@ __device__ inline void block_scan(float v, float* red, float* incl, float* excl,
   *total = tot;
 }
 
-// Loads vocabulary chunk [c0, c1) of one node into LDS: target probabilities
-// p(v) = 2^((z(v) - m) k - ls) at pc[v - c0] and, when want_q, q(v) at
-// qc[v - c0].  VEC: the row is 16-byte aligned and V % 8 == 0, so a group of 8
-// entries never straddles the chunk end.
-template <bool BF16, bool VEC>
-__device__ inline void load_chunk(const void* zrow, const float* qrow, int c0, int c1, float m,
-                                  float k, float ls, bool want_q, float* pc, float* qc) {
-  const int len = c1 - c0;
-  for (int i = threadIdx.x * 8; i < len; i += kAccThreads * 8) {
-    float z[8], q[8];
-    if (VEC) {
-      if (BF16) {
-        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(zrow) + c0 + i);
-        z[0] = bf16_lo(w.x); z[1] = bf16_hi(w.x); z[2] = bf16_lo(w.y); z[3] = bf16_hi(w.y);
-        z[4] = bf16_lo(w.z); z[5] = bf16_hi(w.z); z[6] = bf16_lo(w.w); z[7] = bf16_hi(w.w);
-      } else {
-        const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(zrow) + c0 + i);
-        const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(zrow) + c0 + i + 4);
-        z[0] = a.x; z[1] = a.y; z[2] = a.z; z[3] = a.w; z[4] = b.x; z[5] = b.y; z[6] = b.z; z[7] = b.w;
-      }
-      if (want_q) {
-        const float4 a = *reinterpret_cast<const float4*>(qrow + c0 + i);
-        const float4 b = *reinterpret_cast<const float4*>(qrow + c0 + i + 4);
-        q[0] = a.x; q[1] = a.y; q[2] = a.z; q[3] = a.w; q[4] = b.x; q[5] = b.y; q[6] = b.z; q[7] = b.w;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = c0 + i + e;
-        z[e] = -INFINITY;
-        q[e] = 0.f;
-        if (i + e < len) {
-          z[e] = BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(zrow)[v] << 16)
-                      : reinterpret_cast<const float*>(zrow)[v];
-          if (want_q) q[e] = qrow[v];
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (VEC || i + e < len) {
-        pc[i + e] = z[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(z[e] - m, k, -ls));
-        qc[i + e] = want_q ? q[e] : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-struct GroupSync {
-  int* counter;
+// Group exchange without a shared counter.  Each workgroup publishes up to
+// kXWords values per exchange as 64-bit words (exchange number << 32 | value
+// bits), each written by one atomic store, so a reader that sees the current
+// exchange number in a word also sees that word's value.  Exchange e uses
+// parity slot e % 2; a slot is rewritten at exchange e + 2, which no member
+// reaches before every member has published e + 1, i.e. has finished
+// reading e.  Every word is zeroed at the start of a call and exchange
+// numbers start at 1, so words from earlier calls never match.
+constexpr int kXWords = 3;
+struct GroupXchg {
+  uint64_t* words;  // this group's [2][nchunk][kXWords]
+  int nchunk;
   int epoch;
-  int members;
-  // Returns false when the wait exceeded its bound (co-residency broken).
-  __device__ bool arrive_and_wait() {
+  __device__ uint64_t* slot(int e) const { return words + (size_t)(e & 1) * nchunk * kXWords; }
+  // Thread 0 publishes v[0..nv) for workgroup w; threads below nchunk * nv
+  // each wait for one member's word and put its value in out[member * nv + j].
+  // Returns false when a wait exceeded its bound (co-residency broken).
+  __device__ bool exchange(int w, const float* v, int nv, float* out) {
     __shared__ int ok;
     ++epoch;
+    uint64_t* sl = slot(epoch);
+    const uint64_t tag = (uint64_t)(uint32_t)epoch << 32;
     if (threadIdx.x == 0) {
-      __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      const int target = epoch * members;
-      int spins = 0;
       ok = 1;
-      while (__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-        __builtin_amdgcn_s_sleep(2);
+      for (int j = 0; j < nv; ++j)
+        __hip_atomic_store(sl + (size_t)w * kXWords + j, tag | __float_as_uint(v[j]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < nchunk * nv) {
+      const int m = t / nv, j = t % nv;
+      uint64_t* wp = sl + (size_t)m * kXWords + j;
+      uint64_t x = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int spins = 0;
+      while ((x >> 32) != (uint64_t)(uint32_t)epoch) {
+        __builtin_amdgcn_s_sleep(1);
         if (++spins > (1 << 24)) { ok = 0; break; }
+        x = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      out[t] = __uint_as_float((uint32_t)x);
     }
     __syncthreads();
     return ok != 0;
   }
 };
 
+// Cooperative launch of groups of `nchunk` workgroups; a group walks one
+// sequence at a time, workgroup w owning vocabulary chunk w.  All workgroups
+// of a group take the same scalar decisions from the same exchanged values.
+// At every node the walk visits, the group first forms the statistics of the
+// node's row (one exchange); each rejection then needs the mass of the new
+// residual over the vocabulary (one exchange each).  Only the rows of visited
+// nodes are read.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
   // Per-sequence data gathered once into LDS, so the walk's scalar decisions
@@ -365,17 +366,18 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
   __shared__ int par_s[kMaxT];
   __shared__ int tok_s[kMaxT];
   __shared__ int path_s[kMaxT];
-  __shared__ float m_s[kMaxT];    // row max of the target logits
-  __shared__ float ls_s[kMaxT];   // log2 of sum exp((z - m) / tau) (stochastic rows)
-  __shared__ int am_s[kMaxT];     // lowest-index argmax (greedy rows)
   __shared__ float zx_s[kMaxT];   // logit of node c's token in its parent's row
   __shared__ float qx_s[kMaxT];   // q of node c's token in its parent's row
   __shared__ float ua_s[kMaxT];
   __shared__ float us_s[kMaxT];
   __shared__ float red[kAccThreads / 64];
+  __shared__ float red_m[kAccThreads / 64], red_s[kAccThreads / 64];
+  __shared__ int red_i[kAccThreads / 64], red_f[kAccThreads / 64];
   __shared__ float masses[64];
-  __shared__ float bcast;
-  __shared__ int ibcast;
+  __shared__ float xv[64 * kXWords];   // the group's exchanged values
+  __shared__ float pubv[kXWords];
+  __shared__ float bcast, m_b, ls_b, f_b;
+  __shared__ int ibcast, am_b, bad_b;
   __shared__ int flags_s;
 
   const int tid = threadIdx.x;
@@ -384,8 +386,9 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
   const int c0 = w * p.chunk;
   const int c1 = min(c0 + p.chunk, p.V);
   const bool wor = p.sibling_mode == SV_SIB_WITHOUT_REPLACEMENT;
-  GroupSync gs{p.sync + grp, 0, p.nchunk};
-  extern __shared__ __align__(16) float cache_s[];   // p then q of this workgroup's chunk
+  GroupXchg gx{p.xchg + (size_t)grp * 2 * p.nchunk * kXWords, p.nchunk, 0};
+  // this workgroup's chunk: e(v) = 2^((z(v) - m_c) k) of the visited node, then q
+  extern __shared__ __align__(16) float cache_s[];
   float* pc = cache_s;
   float* qc = cache_s + p.chunk;
   const int len = c1 - c0;
@@ -404,36 +407,17 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
     if (tid == 0) flags_s = 0;
     __syncthreads();
     if (st == SV_TREE_OK) {
-      // round 1: tree, tokens, uniforms, per-row statistics
+      // round 1: tree, tokens, uniforms
       for (int i = tid; i < Tb; i += kAccThreads) {
         par_s[i] = p.parent[rowbase + i];
         const int x = p.tokens[rowbase + i];
         tok_s[i] = x;
         ua_s[i] = p.u_accept[rowbase + i];
         us_s[i] = p.u_sample[rowbase + i];
-        int f = (x < 0 || x >= p.V) ? 1 : 0;
-        const float4* srow = p.stats + (rowbase + i) * p.nchunk;
-        float m = -INFINITY, ssum = 0.f;
-        int am = 0;
-        for (int cc = 0; cc < p.nchunk; ++cc) {
-          const float4 v = srow[cc];
-          f |= __float_as_int(v.w) != 0 ? 2 : 0;
-          if (v.x > m) { m = v.x; am = __float_as_int(v.z); }   // first chunk with the max: lowest index
-        }
-        if (!greedy)
-          for (int cc = 0; cc < p.nchunk; ++cc) {
-            const float4 v = srow[cc];
-            ssum += v.y * __builtin_amdgcn_exp2f((v.x - m) * k);
-          }
-        m_s[i] = m;
-        am_s[i] = am;
-        ls_s[i] = greedy ? 0.f : __log2f(ssum);
-        if (f) atomicOr(&flags_s, f);
+        if (x < 0 || x >= p.V) atomicOr(&flags_s, 1);
       }
       __syncthreads();
-      const int f = flags_s;
-      if (f & 1) st = SV_TREE_E_TOKEN;
-      else if (f & 2) st = SV_TREE_E_NONFINITE;
+      if (flags_s & 1) st = SV_TREE_E_TOKEN;
       else if (!greedy && p.q_probs == nullptr) st = SV_TREE_E_NOQ;
       // round 2: each candidate's logit and draft probability in its parent's row
       if (st == SV_TREE_OK && !greedy) {
@@ -447,25 +431,45 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       }
       __syncthreads();
     }
-    if (st != SV_TREE_OK) {
-      if (w == 0) {
-        for (int i = tid; i < p.T_max; i += kAccThreads) { onodes[i] = -1; otoks[i] = -1; }
-        if (tid == 0) {
-          p.out_count[b] = 0;
-          p.status[b] = st;
-          if (p.out_passes) p.out_passes[b] = 0;
-        }
-      }
-      continue;
-    }
-    if (greedy && w != 0) continue;
 
     int n = 0, path_len = 0, passes = 0, emitted = -1, owner = -1;
-    bool sync_ok = true;
-    while (true) {
+    bool sync_ok = true, nonfinite = false;
+    while (st == SV_TREE_OK) {
+      const void* zrow = BF16 ? (const void*)(reinterpret_cast<const uint16_t*>(p.logits) + (rowbase + n) * p.V)
+                              : (const void*)(reinterpret_cast<const float*>(p.logits) + (rowbase + n) * p.V);
+      const float* qrow = greedy ? nullptr : p.q_probs + (rowbase + n) * p.V;
+      // ---- statistics of node n's row: every chunk, one exchange
+      {
+        const float4 loc = chunk_stats<BF16, VEC>(zrow, c0, c1, greedy, k, pc, red_m, red_s, red_i, red_f);
+        if (tid == 0) { pubv[0] = loc.x; pubv[1] = loc.y; pubv[2] = loc.z; }
+        if (!gx.exchange(w, pubv, 3, xv)) { sync_ok = false; break; }
+        if (tid == 0) {
+          float M = -INFINITY, S = 0.f;
+          int I = 0, F = 0;
+          for (int cc = 0; cc < p.nchunk; ++cc) {
+            const float mc = xv[3 * cc], yc = xv[3 * cc + 1];
+            F |= __float_as_int(xv[3 * cc + 2]);
+            if (mc > M) { M = mc; I = __float_as_int(yc); }   // first chunk with the max: lowest index
+          }
+          if (!greedy) {
+            for (int cc = 0; cc < p.nchunk; ++cc) S += xv[3 * cc + 1] * __builtin_amdgcn_exp2f((xv[3 * cc] - M) * k);
+            const float ls = __log2f(S);
+            for (int cc = 0; cc < p.nchunk; ++cc)
+              masses[cc] = xv[3 * cc + 1] * __builtin_amdgcn_exp2f((xv[3 * cc] - M) * k - ls);
+            ls_b = ls;
+            // p(v) = e(v) f on this chunk
+            f_b = __builtin_amdgcn_exp2f((xv[3 * w] - M) * k - ls);
+          }
+          m_b = M;
+          am_b = I;
+          bad_b = F;
+        }
+        __syncthreads();
+      }
+      if (bad_b) { nonfinite = true; break; }
       int acc = -1;
       if (greedy) {
-        const int am = am_s[n];
+        const int am = am_b;
         for (int i = n + 1; i < Tb; ++i)
           if (par_s[i] == n && tok_s[i] == am) { acc = i; break; }
         if (acc >= 0) {
@@ -478,18 +482,9 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
         owner = 0;
         break;
       }
-      const float m = m_s[n], ls = ls_s[n];
-      const void* zrow = BF16 ? (const void*)(reinterpret_cast<const uint16_t*>(p.logits) + (rowbase + n) * p.V)
-                              : (const void*)(reinterpret_cast<const float*>(p.logits) + (rowbase + n) * p.V);
-      const float* qrow = p.q_probs + (rowbase + n) * p.V;
-      // draw masses of P = p_n, from the chunk statistics
-      __syncthreads();
-      if (tid < p.nchunk) {
-        const float4 v = p.stats[(rowbase + n) * p.nchunk + tid];
-        masses[tid] = v.y * __builtin_amdgcn_exp2f((v.x - m) * k - ls);
-      }
+      const float m = m_b, ls = ls_b, f = f_b;
       float A = 0.f, Wn = 1.f, rm = 0.f, Adraw = 0.f;
-      bool loaded = false;
+      bool have_q = false;
       for (int c = n + 1; c < Tb; ++c) {
         if (par_s[c] != n) continue;
         const float qx = qx_s[c];
@@ -504,35 +499,31 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
         }
         // rejection: mass of the new residual over the whole vocabulary
         const float An = A + Wn * ci;
-        if (!loaded) {
-          load_chunk<BF16, VEC>(zrow, qrow, c0, c1, m, k, ls, true, pc, qc);
-          loaded = true;
+        if (!have_q) {
+          load_q_chunk<VEC>(qrow, c0, c1, qc);
+          __syncthreads();
+          have_q = true;
         }
         float part = 0.f;
         for (int i = tid * 4; i < len; i += kAccThreads * 4) {
           if (i + 4 <= len) {
             const float4 pp = *reinterpret_cast<const float4*>(pc + i);
             const float4 qq = *reinterpret_cast<const float4*>(qc + i);
-            part += fmaxf(fmaf(-An, qq.x, pp.x), 0.f) + fmaxf(fmaf(-An, qq.y, pp.y), 0.f) +
-                    fmaxf(fmaf(-An, qq.z, pp.z), 0.f) + fmaxf(fmaf(-An, qq.w, pp.w), 0.f);
+            part += fmaxf(fmaf(-An, qq.x, pp.x * f), 0.f) + fmaxf(fmaf(-An, qq.y, pp.y * f), 0.f) +
+                    fmaxf(fmaf(-An, qq.z, pp.z * f), 0.f) + fmaxf(fmaf(-An, qq.w, pp.w * f), 0.f);
           } else {
-            for (int e = i; e < len; ++e) part += fmaxf(fmaf(-An, qc[e], pc[e]), 0.f);
+            for (int e = i; e < len; ++e) part += fmaxf(fmaf(-An, qc[e], pc[e] * f), 0.f);
           }
         }
         part = block_sum(part, red);
-        // partials of barrier epoch e live in slot e % 2: a slot is rewritten
-        // two epochs later, after every member has passed the epoch between
-        float* slot = p.part + ((size_t)grp * 2 + ((gs.epoch + 1) & 1)) * p.nchunk;
-        if (tid == 0) __hip_atomic_store(slot + w, part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!gs.arrive_and_wait()) { sync_ok = false; break; }
+        if (tid == 0) pubv[0] = part;
+        if (!gx.exchange(w, pubv, 1, xv)) { sync_ok = false; break; }
         if (tid == 0) {
           float tot = 0.f;
-          for (int cc = 0; cc < p.nchunk; ++cc)
-            tot += __hip_atomic_load(slot + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int cc = 0; cc < p.nchunk; ++cc) tot += xv[cc];
           bcast = tot;
           if (tot > 0.f)
-            for (int cc = 0; cc < p.nchunk; ++cc)
-              masses[cc] = __hip_atomic_load(slot + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int cc = 0; cc < p.nchunk; ++cc) masses[cc] = xv[cc];
         }
         __syncthreads();
         const float Wsum = bcast;
@@ -573,7 +564,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       const bool fallback = owner < 0;
       if (fallback) owner = last_pos < 0 ? 0 : last_pos;
       if (w == owner) {
-        if (!loaded) load_chunk<BF16, VEC>(zrow, qrow, c0, c1, m, k, ls, false, pc, qc);
+        // residual entry i of the chunk (q is only needed after a rejection)
+        auto resid = [&](int i) { return have_q ? fmaxf(fmaf(-Adraw, qc[i], pc[i] * f), 0.f) : pc[i] * f; };
         // scan the chunk in vocabulary order: thread t owns the contiguous
         // segment [t * seg, (t + 1) * seg)
         const int seg = (len + kAccThreads - 1) / kAccThreads;
@@ -581,7 +573,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
         int y = -1;
         if (!fallback) {
           float vs = 0.f;
-          for (int i = s0; i < s1; ++i) vs += fmaxf(fmaf(-Adraw, qc[i], pc[i]), 0.f);
+          for (int i = s0; i < s1; ++i) vs += resid(i);
           float incl, excl, tot;
           block_scan(vs, red, &incl, &excl, &tot);
           if (tid == 0) ibcast = 0x7FFFFFFF;
@@ -590,7 +582,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
             float run = cum + excl;
             int found = -1, lastin = -1;
             for (int i = s0; i < s1; ++i) {
-              const float v = fmaxf(fmaf(-Adraw, qc[i], pc[i]), 0.f);
+              const float v = resid(i);
               if (v > 0.f) lastin = i;
               run += v;
               if (run > target) { found = i; break; }
@@ -605,7 +597,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
           // rounding left no crossing: the largest entry of the chunk with positive mass
           int lp = -1;
           for (int i = s0; i < s1; ++i)
-            if (fmaxf(fmaf(-Adraw, qc[i], pc[i]), 0.f) > 0.f) lp = c0 + i;
+            if (resid(i) > 0.f) lp = c0 + i;
           __syncthreads();
           if (tid == 0) ibcast = -1;
           __syncthreads();
@@ -621,7 +613,19 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       if (tid == 0) p.status[b] = SV_TREE_E_SYNC;
       return;
     }
+    if (nonfinite) st = SV_TREE_E_NONFINITE;
     __syncthreads();
+    if (st != SV_TREE_OK) {
+      if (w == 0) {
+        for (int i = tid; i < p.T_max; i += kAccThreads) { onodes[i] = -1; otoks[i] = -1; }
+        if (tid == 0) {
+          p.out_count[b] = 0;
+          p.status[b] = st;
+          if (p.out_passes) p.out_passes[b] = 0;
+        }
+      }
+      continue;
+    }
     // outputs: the emitted token by its owner, everything else by workgroup 0
     if (w == owner && tid == 0) otoks[path_len] = emitted;
     if (w == 0) {
@@ -667,14 +671,9 @@ bool plan_accept(const sv_tree* t, const sv_accept_args* a, AcceptPlan* pl) {
   if (ngroups < 1) ngroups = 1;
   if (ngroups > t->B) ngroups = t->B > 0 ? t->B : 1;
   pl->ngroups = ngroups;
-  pl->stats_threads = kAccThreads;
   size_t off = 0;
-  pl->off_stats = off;
-  off += align_up((size_t)t->B * t->T_max * nchunk * sizeof(float4), kWsAlign);
-  pl->off_sync = off;
-  off += align_up((size_t)ngroups * sizeof(int), kWsAlign);
-  pl->off_part = off;
-  off += align_up((size_t)ngroups * 2 * nchunk * sizeof(float), kWsAlign);
+  pl->off_xchg = off;
+  off += align_up((size_t)ngroups * 2 * nchunk * kXWords * sizeof(uint64_t), kWsAlign);
   pl->ws_bytes = off;
   return true;
 }
@@ -683,35 +682,6 @@ sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_
                         const AcceptPlan& pl, void* ws, hipStream_t s) {
   if (t->B == 0) return SV_OK;
   char* wsb = static_cast<char*>(ws);
-  StatsParams sp{};
-  sp.logits = a->target_logits;
-  sp.temperature = a->temperature;
-  sp.num_nodes = t->num_nodes;
-  sp.status = tree_status;
-  sp.stats = reinterpret_cast<float4*>(wsb + pl.off_stats);
-  sp.sync = reinterpret_cast<int*>(wsb + pl.off_sync);
-  sp.B = t->B;
-  sp.T_max = t->T_max;
-  sp.V = a->V;
-  sp.nchunk = pl.nchunk;
-  sp.chunk = pl.chunk;
-  sp.ngroups = pl.ngroups;
-  sp.bf16 = a->logit_dtype == SV_BF16;
-  const bool vec = (a->V % 8) == 0 &&
-                   (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0;
-  dim3 grid(pl.nchunk, t->B * t->T_max);
-  if (sp.bf16) {
-    if (vec) hipLaunchKernelGGL((k_vocab_stats<true, true>), grid, dim3(kAccThreads), 0, s, sp);
-    else hipLaunchKernelGGL((k_vocab_stats<true, false>), grid, dim3(kAccThreads), 0, s, sp);
-  } else {
-    if (vec) hipLaunchKernelGGL((k_vocab_stats<false, true>), grid, dim3(kAccThreads), 0, s, sp);
-    else hipLaunchKernelGGL((k_vocab_stats<false, false>), grid, dim3(kAccThreads), 0, s, sp);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_error("vocab stats launch: %s", hipGetErrorString(e));
-    return SV_E_HIP;
-  }
   WalkParams wp{};
   wp.parent = t->parent;
   wp.num_nodes = t->num_nodes;
@@ -726,20 +696,28 @@ sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_
   wp.out_nodes = a->out_nodes;
   wp.out_count = a->out_count;
   wp.out_passes = a->out_passes;
-  wp.stats = sp.stats;
-  wp.sync = sp.sync;
-  wp.part = reinterpret_cast<float*>(wsb + pl.off_part);
+  wp.xchg = reinterpret_cast<uint64_t*>(wsb + pl.off_xchg);
   wp.B = t->B;
   wp.T_max = t->T_max;
   wp.V = a->V;
   wp.nchunk = pl.nchunk;
   wp.chunk = pl.chunk;
   wp.ngroups = pl.ngroups;
-  wp.bf16 = sp.bf16;
+  wp.bf16 = a->logit_dtype == SV_BF16;
   wp.sibling_mode = a->sibling_mode;
-  const bool wvec = vec && (reinterpret_cast<uintptr_t>(a->q_probs) % 16) == 0;
-  const void* fn = sp.bf16 ? (wvec ? (const void*)k_accept_walk<true, true> : (const void*)k_accept_walk<true, false>)
-                           : (wvec ? (const void*)k_accept_walk<false, true> : (const void*)k_accept_walk<false, false>);
+  // exchange words start at zero on every call (a fill kernel: no memset
+  // node, so the call can be captured in a graph)
+  hipLaunchKernelGGL(k_accept_clear, dim3(1), dim3(256), 0, s, wp.xchg, pl.ngroups * 2 * pl.nchunk * kXWords);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("accept clear launch: %s", hipGetErrorString(e));
+    return SV_E_HIP;
+  }
+  // 16-byte vector loads: V % 8 == 0 and 16-byte aligned rows of logits and q
+  const bool vec = (a->V % 8) == 0 && (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a->q_probs) % 16) == 0;
+  const void* fn = wp.bf16 ? (vec ? (const void*)k_accept_walk<true, true> : (const void*)k_accept_walk<true, false>)
+                           : (vec ? (const void*)k_accept_walk<false, true> : (const void*)k_accept_walk<false, false>);
   void* args[] = {&wp};
   const size_t smem = 2 * (size_t)pl.chunk * sizeof(float);
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * kMaxChunk * sizeof(float)));

@@ -49,8 +49,7 @@ struct AcceptPlan {
   int nchunk;       // vocabulary chunks per row (= workgroups per sequence in the walk)
   int chunk;        // tokens per chunk (multiple of 8)
   int ngroups;      // sequence groups resident at once in the walk
-  int stats_threads;
-  size_t off_stats, off_sync, off_part;
+  size_t off_xchg;
   size_t ws_bytes;
 };
 bool plan_accept(const sv_tree* t, const sv_accept_args* a, AcceptPlan* p);

@@ -89,23 +89,32 @@ def test_accept_fuzz(seed):
 
 def test_accept_malformed_inputs():
     need_gpu()
-    inst = make_instance(_spec(cfg_id=220, B=7, tau=1.0, V=3000), 9, with_attn=False)
+    inst = make_instance(_spec(cfg_id=220, B=8, tau=1.0, V=3000), 9, with_attn=False)
+    # rows the clean walk never reads (neither the root, nor an accepted node)
+    _, _, _, status0 = oracle.tree_mask(inst.parent, inst.num_nodes, inst.T_max)
+    clean = oracle.spec_accept(inst.parent, inst.num_nodes, inst.tokens, inst.target_logits, "bf16",
+                               inst.q_probs, inst.temperature, inst.u_accept, inst.u_sample, status0)
+    visited7 = {0} | set(clean["walks"][7]["nodes"])
+    unvisited7 = [n for n in range(int(inst.num_nodes[7])) if n not in visited7]
+    assert unvisited7, "sequence 7 must have a node the walk skips"
     inst.parent[0, 1] = 3                         # tree error
     inst.tokens[1, 1] = inst.V                    # token out of range
     inst.tokens[2, 0] = -1                        # root token out of range
-    nf = np.float32(np.nan)
-    bits = {"bf16": {"nan": 0x7FC0, "inf": 0x7F80, "-inf": 0xFF80}}
-    inst.target_logits[3, 0, 17] = bits["bf16"]["nan"]
-    inst.target_logits[4, int(inst.num_nodes[4]) - 1, 5] = bits["bf16"]["inf"]
-    inst.target_logits[5, 0, 4095 % inst.V] = bits["bf16"]["-inf"]
+    bits = {"nan": 0x7FC0, "inf": 0x7F80, "-inf": 0xFF80}
+    inst.target_logits[3, 0, 17] = bits["nan"]                       # the root row is always read
+    inst.target_logits[4, int(inst.num_nodes[4]) - 1, 5] = bits["inf"]  # read only if visited
+    inst.target_logits[5, 0, 4095 % inst.V] = bits["-inf"]
     # a non-finite value past the tree is never read
     if int(inst.num_nodes[6]) < inst.T_max:
-        inst.target_logits[6, inst.T_max - 1, 3] = bits["bf16"]["nan"]
+        inst.target_logits[6, inst.T_max - 1, 3] = bits["nan"]
+    inst.target_logits[7, unvisited7[-1], 11] = bits["nan"]          # a row the walk never reads
     res, ref, _ = _run(inst, "malformed")
-    assert res["status"][:6].tolist() == [oracle.TREE_E_PARENT, oracle.TREE_E_TOKEN, oracle.TREE_E_TOKEN,
-                                          oracle.TREE_E_NONFINITE, oracle.TREE_E_NONFINITE,
+    assert res["status"][:4].tolist() == [oracle.TREE_E_PARENT, oracle.TREE_E_TOKEN, oracle.TREE_E_TOKEN,
                                           oracle.TREE_E_NONFINITE]
-    assert res["status"][6] == 0
+    assert res["status"][5] == oracle.TREE_E_NONFINITE
+    assert res["status"][4] == ref["status"][4]
+    assert res["status"][6] == 0 and res["status"][7] == 0
+    np.testing.assert_array_equal(res["out_tokens"][7], clean["out_tokens"][7])
 
 
 def test_accept_without_draft_probabilities():
