@@ -40,19 +40,25 @@ COPY_KERNEL = "neg_kernel"
 ATTN_SRC = os.path.join(ROOT, "eagle_tree_verification_attn_amd", "csrc", "attn.hip")
 
 
-def algorithmic_work(inst):
-    """Algorithmic attention flops / bytes and accept bytes of one step.
-
-    Attention: 4 * D flops per (query head, visible key) pair -- QK^T and PV --
-    over L_b prefix keys plus depth+1 ancestor keys per position; bytes = the
-    prefix K and V once, Q in, O out, tree K/V once, mask words.
-    Accept (statistics pass): every logits row of every position once.
-    """
+def tree_depths(parent, num_nodes):
+    """Depth of every node (root 0) from the parent arrays (parents precede children)."""
     import numpy as np
-    import oracle  # noqa: F401  (the oracle's mask gives the depths)
+    depth = np.zeros(parent.shape, dtype=np.int64)
+    for b in range(parent.shape[0]):
+        for i in range(1, int(num_nodes[b])):
+            depth[b, i] = depth[b, int(parent[b, i])] + 1
+    return depth
+
+
+def algorithmic_work(inst):
+    """Algorithmic attention flops and bytes of one step.
+
+    4 * D flops per (query head, visible key) pair -- QK^T and PV -- over L_b
+    prefix keys plus depth+1 ancestor keys per position; bytes = the prefix K
+    and V once, Q in, O out, tree K/V once, mask words.
+    """
     s = 2 if inst.dtype == "bf16" else 4
-    sz = 2 if inst.logit_dtype == "bf16" else 4
-    _, _, depth, _ = oracle.tree_mask(inst.parent, inst.num_nodes, inst.T_max)
+    depth = tree_depths(inst.parent, inst.num_nodes)
     pairs = 0
     for b in range(inst.B):
         T = int(inst.num_nodes[b])
@@ -63,8 +69,17 @@ def algorithmic_work(inst):
                             + 2 * inst.Hq * inst.D * int(inst.num_nodes.sum())
                             + 2 * inst.Hkv * inst.D * int(inst.num_nodes.sum()))
                        + 8 * inst.B * inst.T_max * W)
-    stats_bytes = float(sz * inst.V * int(inst.num_nodes.sum()))
-    return flops, attn_bytes, stats_bytes
+    return flops, attn_bytes
+
+
+def accept_bytes(inst, res):
+    """Bytes the accept step reads: the logits row of every visited node (the
+    root and the accepted nodes) and the draft row of the visited nodes with a
+    rejection, counted as min(passes, visited) rows per sequence."""
+    sz = 2 if inst.logit_dtype == "bf16" else 4
+    visited = res["out_count"].astype(float)
+    q_rows = [min(float(p), v) for p, v in zip(res["out_passes"], visited)]
+    return float(sz * inst.V * visited.sum() + 4 * inst.V * sum(q_rows))
 
 
 def time_launches(fn, n, stream):
@@ -247,15 +262,11 @@ def main():
     attn_ms = time_launches(dev.tree_attn, n, stream)
     acc_ms = time_launches(dev.spec_accept, n, stream)
     res = dev.accept_results()
-    flops, attn_bytes, stats_bytes = algorithmic_work(inst)
+    flops, attn_bytes = algorithmic_work(inst)
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
-    # accept bytes: every logits row once, plus one (logits row, q row) read per
-    # vocabulary pass of the walk
-    sz = 2 if inst.logit_dtype == "bf16" else 4
-    walk_bytes = float(int(res["out_passes"].sum()) * inst.V * (sz + 4))
-    acc_bytes = stats_bytes + walk_bytes
+    acc_bytes = accept_bytes(inst, res)
     acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
     traffic = counters_traffic()
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -68,7 +68,7 @@ enum {
   SV_TREE_E_PARENT = 2,    /* some 1 <= i < T_b has parent[b][i] outside [0, i)       */
   SV_TREE_E_COUNT = 3,     /* num_nodes[b] outside [1, T_max]                         */
   SV_TREE_E_TOKEN = 4,     /* some tokens[b][i], i < T_b, outside [0, V)              */
-  SV_TREE_E_NONFINITE = 5, /* a NaN or +-Inf in target_logits[b][0..T_b)              */
+  SV_TREE_E_NONFINITE = 5, /* a NaN or +-Inf in the logits row of a node the walk visits */
   SV_TREE_E_NOQ = 6,       /* temperature[b] > 0 but q_probs is NULL                  */
   SV_TREE_E_SYNC = 7       /* internal: a cross-workgroup wait timed out              */
 };
@@ -166,6 +166,9 @@ sv_status sv_tree_attn(const sv_tree* tree, const uint64_t* anc, const int32_t* 
  * Outputs: out_nodes = accepted positions, out_tokens = their tokens followed
  * by the emitted token, out_count = accepted + 1.  tree_status[b] may be set to
  * SV_TREE_E_TOKEN, _NONFINITE, _NOQ or _SYNC (then outputs are -1 / count 0).
+ * Only the logits rows of the nodes the walk visits (the root and the accepted
+ * nodes) are read, and only those are checked for NaN / infinity; draft rows
+ * are read for the visited nodes with a rejection.
  *   ws / ws_bytes: at least sv_workspace_bytes(tree, NULL, a) bytes, 256-byte
  *   aligned.  The walk kernel is a cooperative launch; calls that overlap on
  *   one device must use different workspaces. */
