@@ -225,7 +225,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int W = p.W;
   for (int i = tid; i < p.T_max * W; i += NTHR) anc_s[i] = p.anc[(size_t)b * p.T_max * W + i];
 
-  // queries -> registers (B operand of the score MFMA)
+  // queries -> registers (B operand of the score MFMA), multiplied by
+  // scale * log2(e) and rounded to bf16 once, so the MFMA yields scores in
+  // log2 units (relative error 2^-9 per element of q: about 0.1% on p for
+  // unit-variance data, below the bf16 rounding of p itself)
   bf16x8 qreg[NT][DK];
 #pragma unroll
   for (int qt = 0; qt < NT; ++qt) {
@@ -234,7 +237,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int t = r / G, h = kvh * G + r % G;
       const __bf16* src = qp + (((size_t)b * p.T_max + t) * p.Hq + h) * D + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) qreg[qt][kk] = *reinterpret_cast<const bf16x8*>(src + 32 * kk);
+      for (int kk = 0; kk < DK; ++kk) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 32 * kk);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = pack_bf16x2((float)x[2 * e] * p.scale_log2, (float)x[2 * e + 1] * p.scale_log2);
+        qreg[qt][kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < DK; ++kk) qreg[qt][kk] = bf16x8{};
@@ -243,16 +253,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // acc: O^T tiles; lsum: the row sums of P, accumulated by an MFMA with an
   // all-ones A operand, so every element of lsum[qt] holds its column's sum.
-  // m_run is in log2 units; thr is the raw score above which the running max
-  // must be raised (m_run + 8 in raw units), mu the exp2 offset.
-  f32x4 acc[NT][DT], lsum[NT];
-  float m_run[NT], thr[NT], mu[NT];
-  const float inv_scale_log2 = 1.f / p.scale_log2;
+  // mu: the running exp2 offset of the lane's row (log2 units), subtracted by
+  // the score MFMA itself (its accumulator starts at cinit = -mu); valid once
+  // a visible key has set it.  P = 2^(score - mu) with score - mu <= 8 kept.
+  f32x4 acc[NT][DT], lsum[NT], cinit[NT];
+  float mu[NT];
+  bool valid[NT];
 #pragma unroll
   for (int qt = 0; qt < NT; ++qt) {
-    m_run[qt] = -INFINITY;
-    thr[qt] = -INFINITY;
     mu[qt] = 0.f;
+    valid[qt] = false;
+    cinit[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -352,7 +363,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int qt = 0; qt < NT; ++qt)
           s[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              a, qreg[qt][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[qt][kt], 0, 0, 0);
+              a, qreg[qt][kk], kk == 0 ? cinit[qt] : s[qt][kt], 0, 0, 0);
       }
     }
 
@@ -389,32 +400,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
 
-    // ---- online softmax (exp2, scale folded), P packed to bf16 for the PV MFMA.
-    // Each lane compares its own 8 raw scores per tile with the threshold; only
-    // when some lane exceeds it (rare once the first blocks are seen) does the
-    // wave form the column maxima and raise the running maxima.
-    bool need_any = false;
-    float pm[NT];
+    // ---- online softmax, P packed to bf16 for the PV MFMA.  The scores
+    // already are score - mu in log2 units.  Each lane compares the maximum of
+    // its 24 values with the bound 8; only when some lane exceeds it, or a row
+    // has no offset yet, does the wave form column maxima and raise offsets.
+    float pmax = -INFINITY;
+    bool unset = false;
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
-      const float a0 = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
-      const float a1 = fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]));
-      pm[qt] = fmaxf(a0, a1);
-      need_any |= pm[qt] > thr[qt];
+      pmax = fmaxf(pmax, fmaxf(fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3])),
+                               fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]))));
+      unset |= !valid[qt];
     }
-    if (__any(need_any)) {
+    if (__any(pmax > 8.0f || unset)) {
 #pragma unroll
       for (int qt = 0; qt < NT; ++qt) {
-        const float mx = col_max4(pm[qt]) * p.scale_log2;
-        const bool need = mx > m_run[qt] + 8.0f;
-        const float mnew = need ? mx : m_run[qt];
-        const float alpha = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - mnew);
+        const float a0 = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
+        const float a1 = fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]));
+        const float cm = col_max4(fmaxf(a0, a1));   // column max of score - mu
+        // a row without an offset takes the first visible maximum (its
+        // accumulators are still zero); a row with one raises it past 8
+        const bool raise = valid[qt] ? cm > 8.0f : cm > -INFINITY;
+        if (raise) {
+          if (valid[qt]) {
+            const float alpha = __builtin_amdgcn_exp2f(-cm);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
-        lsum[qt] *= alpha;
-        m_run[qt] = mnew;
-        mu[qt] = mnew == -INFINITY ? 0.f : mnew;
-        thr[qt] = mnew == -INFINITY ? -INFINITY : (mnew + 8.0f) * inv_scale_log2;
+            for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
+            lsum[qt] *= alpha;
+          }
+          mu[qt] += cm;
+          valid[qt] = true;
+          cinit[qt] = f32x4{-mu[qt], -mu[qt], -mu[qt], -mu[qt]};
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) s[qt][kt] -= cm;
+        }
       }
     }
     bf16x8 pk[NT];
@@ -424,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[kt * 4 + i] = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][i], p.scale_log2, -mu[qt]));
+        for (int i = 0; i < 4; ++i) pv[kt * 4 + i] = __builtin_amdgcn_exp2f(s[qt][kt][i]);
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
@@ -472,7 +491,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             make_float4(acc[qt][dt][0], acc[qt][dt][1], acc[qt][dt][2], acc[qt][dt][3]);
       if (g == 0) {
         float* pm = p.part_ml + (orow * p.lsplit + ls_i) * 2;
-        pm[0] = m_run[qt];
+        pm[0] = valid[qt] ? mu[qt] : -INFINITY;
         pm[1] = l;
       }
     }
