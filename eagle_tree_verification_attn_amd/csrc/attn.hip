@@ -106,7 +106,7 @@ __device__ inline bf16x4 lds_read_tr16(const __bf16* p) {
 // ever set right here.
 __device__ inline void copy16_to_lds(const void* gptr, uint32_t lds_byte_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "s"(lds_byte_addr) : "memory");
+               :: "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr)) : "memory");
 }
 // Wait until at most N of this wave's vector-memory loads are outstanding
 // (they complete in issue order), then join the workgroup barrier.
@@ -132,6 +132,8 @@ __device__ inline int kv_swizzle(int r) {
 // kStages - 1.
 constexpr int kStages = 4;
 
+// Work unit: (sequence b, KV head, block of query rows, range of keys); one
+// workgroup of NW waves per unit, one barrier per key block.
 template <int D, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_bf16(AttnParams p) {
   constexpr int NTHR = NW * 64;
@@ -271,20 +273,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
-  // ---- staging: a ring of kStages (K, V) tile pairs in LDS, filled by direct
-  // copies.  Copy instruction j of wave w fills tile rows [(w IPW + j) RPI,
-  // + RPI); lane l of it loads row l / SEGS, segment (l % SEGS) ^ swizzle(row).
-  // Keys past the range end are clamped to the last valid key (their scores
-  // are masked to -inf, so those rows of V are weighted by exactly 0).
-  int drow[IPW];
-  uint32_t dseg[IPW], doff[IPW];
-#pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    drow[j] = (wave * IPW + j) * RPI + lane / SEGS;
-    dseg[j] = (uint32_t)(((lane % SEGS) ^ kv_swizzle<D>(drow[j])) * 8);
-    doff[j] = (uint32_t)(drow[j] * D) + dseg[j];
-  }
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_byte_address(smem_raw));
+  // ---- staging: a ring of kStages (K, V) tile pairs in LDS, filled
+  // by direct copies.  Copy instruction j of wave w fills tile rows
+  // [(w IPW + j) RPI, + RPI); lane l of it loads row l / SEGS, segment
+  // (l % SEGS) ^ swizzle(row).  Keys past the range end are clamped to the
+  // last valid key (their scores are masked to -inf, so those rows of V are
+  // weighted by exactly 0).
+  // (the lane's copy coordinates are recomputed per block: a few VALU
+  // operations instead of registers held through the loop)
+  auto copy_row = [&](int j) { return (wave * IPW + j) * RPI + lane / SEGS; };
+  auto copy_seg = [&](int j) { return (uint32_t)(((lane % SEGS) ^ kv_swizzle<D>(copy_row(j))) * 8); };
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_byte_address(smem));
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)(wave * IPW * 1024));
   const int fast_end = min(Lb, kend);   // blocks ending here or before are all cache keys
   const uint64_t kc_addr = reinterpret_cast<uint64_t>(kc), vc_addr = reinterpret_cast<uint64_t>(vc);
@@ -298,17 +297,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const __bf16* vb = vc + (size_t)blk * D;
 #pragma unroll
       for (int j = 0; j < IPW; ++j) {
-        copy16_to_lds(kb + doff[j], kl + j * 1024);
-        copy16_to_lds(vb + doff[j], vl + j * 1024);
+        const uint32_t off = (uint32_t)(copy_row(j) * D) + copy_seg(j);
+        copy16_to_lds(kb + off, kl + j * 1024);
+        copy16_to_lds(vb + off, vl + j * 1024);
       }
       return;
     }
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      const int jr = blk + drow[j];
+      const int jr = blk + copy_row(j);
       const int jj = jr < kend ? jr : kend - 1;
       const bool in_cache = jj < Lb;
-      const uint64_t loc = 2ull * ((in_cache ? (uint32_t)jj * D : (uint32_t)(jj - Lb) * new_stride32) + dseg[j]);
+      const uint64_t loc = 2ull * ((in_cache ? (uint32_t)jj * D : (uint32_t)(jj - Lb) * new_stride32) + copy_seg(j));
       const uint64_t ka = (in_cache ? kc_addr : kn_addr) + loc;
       const uint64_t va = (in_cache ? vc_addr : vn_addr) + loc;
       copy16_to_lds(reinterpret_cast<const void*>(ka), kl + j * 1024);
@@ -343,18 +343,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int i = 0; i < kStages - 1; ++i)
     if (i < nblk) issue_block(kbeg + i * BK, i);
 
-  for (int it = 0; it < nblk; ++it) {
-    const int blk = kbeg + it * BK;
-    // block it has landed (for every wave) and every wave is done with block
-    // it - 1, whose ring slot the next copy refills
-    if (it + kStages - 2 < nblk) wait_copies_and_sync<(kStages - 2) * CPB>();
-    else wait_copies_and_sync<0>();
-    if (it + kStages - 1 < nblk) issue_block(blk + (kStages - 1) * BK, (it + kStages - 1) % kStages);
-    const __bf16* ks = smem + (it % kStages) * STAGE;
-    const __bf16* vs = ks + TILE;
-
-    // ---- scores S^T (2 sub-tiles of 16 keys)
-    f32x4 s[NT][2];
+  // ---- scores S^T of key block n (2 sub-tiles of 16 keys), minus mu, masked
+  f32x4 s[NT][2];
+  auto scores = [&](int n) {
+    const int blk = kbeg + n * BK;
+    const __bf16* ks = smem + (n % kStages) * STAGE;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -366,8 +359,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
               a, qreg[qt][kk], kk == 0 ? cinit[qt] : s[qt][kt], 0, 0, 0);
       }
     }
-
-    // ---- mask: keys past the range end, and tree keys that are not ancestors.
+    // mask: keys past the range end, and tree keys that are not ancestors.
     // Visibility of the block's 32 keys for this lane's row, as one word:
     // bit o <=> key blk + o is a prefix key, or a tree key whose node is an
     // ancestor-or-self of the row's node, and lies before kend.
@@ -399,11 +391,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           }
       }
     }
+  };
 
-    // ---- online softmax, P packed to bf16 for the PV MFMA.  The scores
-    // already are score - mu in log2 units.  Each lane compares the maximum of
-    // its 24 values with the bound 8; only when some lane exceeds it, or a row
-    // has no offset yet, does the wave form column maxima and raise offsets.
+  // ---- online softmax of s, P packed to bf16 for the PV MFMA and kept in the
+  // registers of s[qt][0] (so only s lives from one phase to the next).  The
+  // scores already are score - mu in log2 units.  Each lane compares the
+  // maximum of its values with the bound 8; only when some lane exceeds it, or
+  // a row has no offset yet, does the wave form column maxima and raise offsets.
+  auto softmax = [&]() {
     float pmax = -INFINITY;
     bool unset = false;
 #pragma unroll
@@ -436,7 +431,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
       }
     }
-    bf16x8 pk[NT];
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
       float pv[8];
@@ -447,12 +441,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
-      pk[qt] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      s[qt][0] = __builtin_bit_cast(f32x4, make_uint4(w[0], w[1], w[2], w[3]));
     }
+  };
 
-    // ---- O^T += V^T P^T.  Lane (g, c) needs V[key][16 dt + c] for keys
-    // 4g + k and 16 + 4g + k (k = 0..3); as a source of the transposed read it
-    // addresses row 4g + c/4 (+16), dims 16 dt + 4 (c % 4) .. +3.
+  // ---- O^T += V^T P^T for key block n.  Lane (g, c) needs V[key][16 dt + c]
+  // for keys 4g + k and 16 + 4g + k (k = 0..3); as a source of the transposed
+  // read it addresses row 4g + c/4 (+16), dims 16 dt + 4 (c % 4) .. +3.
+  auto pv_product = [&](int n) {
+    const __bf16* vs = smem + (n % kStages) * STAGE + TILE;
+    bf16x8 pk[NT];
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) pk[qt] = __builtin_bit_cast(bf16x8, s[qt][0]);
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt)
       lsum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[qt], lsum[qt], 0, 0, 0);
@@ -465,6 +465,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int qt = 0; qt < NT; ++qt)
         acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[qt], acc[qt][dt], 0, 0, 0);
     }
+  };
+
+  for (int it = 0; it < nblk; ++it) {
+    // block it has landed (for every wave) and every wave is done with block
+    // it - 1, whose ring slot the next copy refills
+    if (it + kStages - 2 < nblk) wait_copies_and_sync<(kStages - 2) * CPB>();
+    else wait_copies_and_sync<0>();
+    if (it + kStages - 1 < nblk) issue_block(kbeg + (it + kStages - 1) * BK, (it + kStages - 1) % kStages);
+    scores(it);
+    softmax();
+    pv_product(it);
   }
 
   // ---- epilogue

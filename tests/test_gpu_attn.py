@@ -96,6 +96,16 @@ def test_attention_key_splits(lsplit, dtype):
     _run(inst, f"lsplit={lsplit} {dtype}", env={"SV_ATTN_LSPLIT": str(lsplit)})
 
 
+@pytest.mark.parametrize("lsplit", ["1", "3"])
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_odd_kv_heads(D, lsplit):
+    """Three KV heads (odd), ragged prefixes including 0, with and without key splits."""
+    need_gpu()
+    spec = _spec(B=3, Hq=12, Hkv=3, D=D, prefix_len=[300, 0, 97], tree=("dynamic", 2, 5, 2, 6, 5, 40))
+    inst = make_instance(spec, 6, with_accept=False)
+    _run(inst, f"odd Hkv D={D} lsplit={lsplit}", env={"SV_ATTN_LSPLIT": lsplit})
+
+
 def test_attention_invalid_sequences_zero():
     need_gpu()
     spec = _spec(B=3, prefix_len=[50, 60, 70], tree=("widths", [2, 2]))
