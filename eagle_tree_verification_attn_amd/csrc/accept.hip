@@ -9,7 +9,7 @@
 // the corrected distribution; only when all k are rejected is the correction
 // sampled; the rule is applied recursively at every node of the tree.
 //
-// One cooperative kernel, k_accept_walk: groups of `nchunk` workgroups, a
+// One kernel, k_accept_walk: groups of `nchunk` workgroups, all resident, a
 // group walking one sequence at a time with workgroup w owning vocabulary
 // chunk w.  At each node the walk visits, every workgroup reads its chunk of
 // the node's logits row once into LDS and the group combines the chunk
@@ -339,10 +339,11 @@ struct GroupXchg {
       const int m = t / nv, j = t % nv;
       uint64_t* wp = sl + (size_t)m * kXWords + j;
       uint64_t x = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int spins = 0;
+      // bounded by time (the 100 MHz real-time counter): 2 s
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       while ((x >> 32) != (uint64_t)(uint32_t)epoch) {
         __builtin_amdgcn_s_sleep(1);
-        if (++spins > (1 << 24)) { ok = 0; break; }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull) { ok = 0; break; }
         x = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       out[t] = __uint_as_float((uint32_t)x);
@@ -352,7 +353,8 @@ struct GroupXchg {
   }
 };
 
-// Cooperative launch of groups of `nchunk` workgroups; a group walks one
+// Groups of `nchunk` workgroups, all resident at once (the grid is at most one
+// workgroup per CU, checked on the host); a group walks one
 // sequence at a time, workgroup w owning vocabulary chunk w.  All workgroups
 // of a group take the same scalar decisions from the same exchanged values.
 // At every node the walk visits, the group first forms the statistics of the
@@ -721,8 +723,27 @@ sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_
   void* args[] = {&wp};
   const size_t smem = 2 * (size_t)pl.chunk * sizeof(float);
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * kMaxChunk * sizeof(float)));
-  if (e == hipSuccess)
-    e = hipLaunchCooperativeKernel(fn, dim3(pl.ngroups * pl.nchunk), dim3(kAccThreads), args, smem, s);
+  // The workgroups of a group wait for each other, so the whole grid must fit
+  // on the device at once: at most one workgroup per CU, and the kernel's
+  // occupancy must allow one.  (A plain launch: the cooperative one costs
+  // about 20 us more per call.)  Workgroups queued behind other work on the
+  // device start when that work ends; the waits are bounded by time and
+  // report SV_TREE_E_SYNC rather than hang.
+  static int occ_cache[64][4];   // per device and kernel variant, 0 = not asked yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int& occ = occ_cache[dev][(wp.bf16 ? 2 : 0) + (vec ? 1 : 0)];
+  if (e == hipSuccess && occ == 0) {
+    // the smallest chunk size needs the least LDS: ask with the largest
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAccThreads, 2 * kMaxChunk * sizeof(float));
+    if (e == hipSuccess && occ == 0) occ = -1;
+  }
+  if (e == hipSuccess && (occ < 1 || pl.ngroups * pl.nchunk > device_info().num_cu)) {
+    set_error("accept walk: %d workgroups do not fit at once (%d per CU, %d CUs)", pl.ngroups * pl.nchunk, occ,
+              device_info().num_cu);
+    return SV_E_UNSUPPORTED;
+  }
+  if (e == hipSuccess) e = hipLaunchKernel(fn, dim3(pl.ngroups * pl.nchunk), dim3(kAccThreads), args, smem, s);
   if (e != hipSuccess) {
     set_error("accept walk launch: %s", hipGetErrorString(e));
     return SV_E_HIP;

@@ -170,8 +170,12 @@ sv_status sv_tree_attn(const sv_tree* tree, const uint64_t* anc, const int32_t* 
  * nodes) are read, and only those are checked for NaN / infinity; draft rows
  * are read for the visited nodes with a rejection.
  *   ws / ws_bytes: at least sv_workspace_bytes(tree, NULL, a) bytes, 256-byte
- *   aligned.  The walk kernel is a cooperative launch; calls that overlap on
- *   one device must use different workspaces. */
+ *   aligned.  The walk kernel's workgroups (at most one per CU) wait for one
+ *   another, so all of them must be resident together: on a device shared with
+ *   other work, workgroups queued behind it start when it ends; a wait longer
+ *   than 2 s reports SV_TREE_E_SYNC.  Calls that overlap on one device must
+ *   use different workspaces.  Returns SV_E_UNSUPPORTED if the grid cannot be
+ *   resident at once. */
 sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_accept_args* a,
                          void* ws, size_t ws_bytes, void* stream);
 
