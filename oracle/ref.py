@@ -49,6 +49,8 @@ TREE_E_COUNT = 3
 TREE_E_TOKEN = 4
 TREE_E_NONFINITE = 5
 TREE_E_NOQ = 6
+TREE_E_SYNC = 7      # device-side only (a cross-workgroup wait timed out)
+TREE_E_CACHE = 8
 
 SIB_WITHOUT_REPLACEMENT = 0
 SIB_IID = 1
@@ -362,6 +364,56 @@ def spec_accept(parent, num_nodes, tokens, target_logits, logit_dtype, q_probs, 
         out_count[b] = w["count"]
     return dict(out_nodes=out_nodes, out_tokens=out_tokens, out_count=out_count, status=status,
                 walks=walks)
+
+
+# --------------------------------------------------------------------------
+# Commit of the accepted path
+#   [EAGLE article, sec. 1.3 "Verification"]: after verification the accepted
+#   tokens and their features are kept and drafting continues from them.
+#   [Spec-decoding lesson, "Concept"]: the accepted tokens extend the output;
+#   the correction / bonus token is the next position to run the target on.
+# Reading: the verified positions whose key/value rows enter the cache are the
+# root (the last emitted token, verified in this pass) and the accepted nodes,
+# in path order; the emitted token is the next root, so its rows come from
+# the next forward pass.
+# --------------------------------------------------------------------------
+def commit_accepted(k_new, v_new, k_cache, v_cache, prefix_len, status_in, out_nodes, out_count,
+                    feat_in=None):
+    """Append the root's and the accepted nodes' K/V rows to the caches.
+
+    k_new, v_new [B][T_max][Hkv][D]; k_cache, v_cache [B][Hkv][L_max][D] (any
+    element type, copied bit for bit); out_nodes [B][T_max], out_count [B] as
+    produced by spec_accept.  For a valid sequence with count c >= 1 the rows
+    of positions [0, out_nodes[b][0], ..., out_nodes[b][c-2]] go to cache rows
+    L_b .. L_b + c - 1 of every KV head and the new length is L_b + c; if that
+    exceeds L_max the sequence gets TREE_E_CACHE and nothing is written.
+    feat_in [B][T_max][F] (optional): the same positions' rows go to rows
+    0 .. c-1 of feat_out (other rows zero).
+    Returns dict(k_cache, v_cache, prefix_len, status, feat_out) (copies).
+    """
+    k_cache = np.array(k_cache, copy=True)
+    v_cache = np.array(v_cache, copy=True)
+    B = k_cache.shape[0]
+    L_max = k_cache.shape[2]
+    new_len = np.array(prefix_len, dtype=np.int32).copy()
+    status = np.array(status_in, dtype=np.int32).copy()
+    feat_out = None if feat_in is None else np.zeros_like(feat_in)
+    for b in range(B):
+        c = int(out_count[b])
+        if status[b] != TREE_OK or c < 1:
+            continue
+        L = int(prefix_len[b])
+        if L + c > L_max:
+            status[b] = TREE_E_CACHE
+            continue
+        positions = [0] + [int(out_nodes[b][i]) for i in range(c - 1)]
+        for i, n in enumerate(positions):
+            k_cache[b, :, L + i, :] = k_new[b, n, :, :]
+            v_cache[b, :, L + i, :] = v_new[b, n, :, :]
+            if feat_out is not None:
+                feat_out[b, i] = feat_in[b, n]
+        new_len[b] = L + c
+    return dict(k_cache=k_cache, v_cache=v_cache, prefix_len=new_len, status=status, feat_out=feat_out)
 
 
 def verify_step(inst, sibling_mode=None, attn_units=None, accept_seqs=None):
