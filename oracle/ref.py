@@ -51,6 +51,7 @@ TREE_E_NONFINITE = 5
 TREE_E_NOQ = 6
 TREE_E_SYNC = 7      # device-side only (a cross-workgroup wait timed out)
 TREE_E_CACHE = 8
+TREE_E_PATH = 9
 
 SIB_WITHOUT_REPLACEMENT = 0
 SIB_IID = 1
@@ -377,8 +378,8 @@ def spec_accept(parent, num_nodes, tokens, target_logits, logit_dtype, q_probs, 
 # in path order; the emitted token is the next root, so its rows come from
 # the next forward pass.
 # --------------------------------------------------------------------------
-def commit_accepted(k_new, v_new, k_cache, v_cache, prefix_len, status_in, out_nodes, out_count,
-                    feat_in=None):
+def commit_accepted(k_new, v_new, k_cache, v_cache, prefix_len, num_nodes, status_in, out_nodes,
+                    out_count, feat_in=None):
     """Append the root's and the accepted nodes' K/V rows to the caches.
 
     k_new, v_new [B][T_max][Hkv][D]; k_cache, v_cache [B][Hkv][L_max][D] (any
@@ -386,7 +387,8 @@ def commit_accepted(k_new, v_new, k_cache, v_cache, prefix_len, status_in, out_n
     produced by spec_accept.  For a valid sequence with count c >= 1 the rows
     of positions [0, out_nodes[b][0], ..., out_nodes[b][c-2]] go to cache rows
     L_b .. L_b + c - 1 of every KV head and the new length is L_b + c; if that
-    exceeds L_max the sequence gets TREE_E_CACHE and nothing is written.
+    exceeds L_max the sequence gets TREE_E_CACHE, and if c > T_b or a path
+    entry lies outside [1, T_b) it gets TREE_E_PATH; then nothing is written.
     feat_in [B][T_max][F] (optional): the same positions' rows go to rows
     0 .. c-1 of feat_out (other rows zero).
     Returns dict(k_cache, v_cache, prefix_len, status, feat_out) (copies).
@@ -403,10 +405,14 @@ def commit_accepted(k_new, v_new, k_cache, v_cache, prefix_len, status_in, out_n
         if status[b] != TREE_OK or c < 1:
             continue
         L = int(prefix_len[b])
-        if L + c > L_max:
+        T_b = int(num_nodes[b])
+        positions = [0] + [int(out_nodes[b][i]) for i in range(c - 1)] if c <= T_b else None
+        if positions is None or any(n < 1 or n >= T_b for n in positions[1:]):
+            status[b] = TREE_E_PATH
+            continue
+        if L < 0 or L + c > L_max:
             status[b] = TREE_E_CACHE
             continue
-        positions = [0] + [int(out_nodes[b][i]) for i in range(c - 1)]
         for i, n in enumerate(positions):
             k_cache[b, :, L + i, :] = k_new[b, n, :, :]
             v_cache[b, :, L + i, :] = v_new[b, n, :, :]

@@ -7,7 +7,8 @@
   definition rather than restated;
 * features cross-check: features taken from the K rows of one head come out
   equal to the rows the commit wrote into that head's cache;
-* special cases: a cache without room, an invalid sequence, the root alone.
+* special cases: a cache without room, an invalid sequence, the root alone,
+  path entries out of range.
 """
 import math
 
@@ -43,7 +44,7 @@ def test_commit_then_causal_attention_reproduces_tree_attention(seed):
     inst = make_instance(_spec(L_max=23 + 22), seed)
     status, att, acc = _verify(inst)
     com = oracle.commit_accepted(inst.k_new, inst.v_new, inst.k_cache, inst.v_cache, inst.prefix_len,
-                                 acc["status"], acc["out_nodes"], acc["out_count"])
+                                 inst.num_nodes, acc["status"], acc["out_nodes"], acc["out_count"])
     G = inst.Hq // inst.Hkv
     scale = 1.0 / math.sqrt(inst.D)
     checked = 0
@@ -75,7 +76,7 @@ def test_commit_features_match_committed_cache_rows():
     h = 1
     feat_in = np.ascontiguousarray(inst.k_new[:, :, h, :])                      # F = D rows of head h
     com = oracle.commit_accepted(inst.k_new, inst.v_new, inst.k_cache, inst.v_cache, inst.prefix_len,
-                                 acc["status"], acc["out_nodes"], acc["out_count"], feat_in)
+                                 inst.num_nodes, acc["status"], acc["out_nodes"], acc["out_count"], feat_in)
     for b in range(inst.B):
         if acc["status"][b] != oracle.TREE_OK:
             continue
@@ -85,7 +86,7 @@ def test_commit_features_match_committed_cache_rows():
 
 
 def test_commit_special_cases():
-    inst = make_instance(_spec(B=3, prefix_len=[10, 3, 6], L_max=12), 3)
+    inst = make_instance(_spec(B=5, prefix_len=[10, 3, 6, 2, 2], L_max=12, tree=("widths", [2, 2])), 3)
     status, _, acc = _verify(inst)
     nodes = acc["out_nodes"].copy()
     count = acc["out_count"].copy()
@@ -95,10 +96,13 @@ def test_commit_special_cases():
     count[1] = 1                  # the root alone
     nodes[1, :] = -1
     st[2] = oracle.TREE_E_PARENT  # invalid sequence: left alone
+    count[3], nodes[3, 0] = 2, 5  # a path entry outside [1, T_b) (T_b = 5)
+    count[4] = 6                  # more than T_b positions
     com = oracle.commit_accepted(inst.k_new, inst.v_new, inst.k_cache, inst.v_cache, inst.prefix_len,
-                                 st, nodes, count)
-    assert com["status"].tolist() == [oracle.TREE_E_CACHE, oracle.TREE_OK, oracle.TREE_E_PARENT]
-    assert com["prefix_len"].tolist() == [10, 4, 6]
+                                 inst.num_nodes, st, nodes, count)
+    assert com["status"].tolist() == [oracle.TREE_E_CACHE, oracle.TREE_OK, oracle.TREE_E_PARENT,
+                                      oracle.TREE_E_PATH, oracle.TREE_E_PATH]
+    assert com["prefix_len"].tolist() == [10, 4, 6, 2, 2]
     np.testing.assert_array_equal(com["k_cache"][0], inst.k_cache[0])
     np.testing.assert_array_equal(com["k_cache"][2], inst.k_cache[2])
     np.testing.assert_array_equal(com["k_cache"][1][:, 3], inst.k_new[1, 0])
