@@ -8,7 +8,7 @@ library fails loudly (build it with ``python -m eagle_tree_verification_attn_amd
 
 Entry points (same names as the C ABI):
     sv_tree_mask_build, sv_tree_attn, sv_spec_accept, sv_verify_step,
-    sv_workspace_bytes, sv_status_string, sv_last_error
+    sv_commit_accepted, sv_workspace_bytes, sv_status_string, sv_last_error
 """
 import ctypes
 import os
@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(_HERE, "libsv.so")
 SV_OK, SV_E_NULL, SV_E_SHAPE, SV_E_DTYPE, SV_E_WORKSPACE, SV_E_HIP, SV_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 SV_TREE_OK, SV_TREE_E_ROOT, SV_TREE_E_PARENT, SV_TREE_E_COUNT = 0, 1, 2, 3
 SV_TREE_E_TOKEN, SV_TREE_E_NONFINITE, SV_TREE_E_NOQ, SV_TREE_E_SYNC = 4, 5, 6, 7
+SV_TREE_E_CACHE, SV_TREE_E_PATH = 8, 9
 SV_F32, SV_BF16 = 0, 1
 SV_SIB_WITHOUT_REPLACEMENT, SV_SIB_IID = 0, 1
 
 EXPORTS = ["sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step",
-           "sv_workspace_bytes", "sv_status_string", "sv_last_error"]
+           "sv_commit_accepted", "sv_workspace_bytes", "sv_status_string", "sv_last_error"]
 
 
 class SvTree(ctypes.Structure):
@@ -47,6 +48,15 @@ class SvAcceptArgs(ctypes.Structure):
                 ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p),
                 ("out_tokens", ctypes.c_void_p), ("out_nodes", ctypes.c_void_p),
                 ("out_count", ctypes.c_void_p), ("out_passes", ctypes.c_void_p)]
+
+
+class SvCommitArgs(ctypes.Structure):
+    _fields_ = [("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("L_max", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("prefix_len", ctypes.c_void_p), ("prefix_len_out", ctypes.c_void_p),
+                ("F", ctypes.c_int32), ("feat_dtype", ctypes.c_int32),
+                ("feat_in", ctypes.c_void_p), ("feat_out", ctypes.c_void_p)]
 
 
 class SvError(RuntimeError):
@@ -75,13 +85,15 @@ def lib():
         L.sv_verify_step.argtypes = [P(SvTree), P(SvAttnArgs), P(SvAcceptArgs), ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
+        L.sv_commit_accepted.argtypes = [P(SvTree), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         P(SvCommitArgs), ctypes.c_void_p]
         L.sv_workspace_bytes.argtypes = [P(SvTree), P(SvAttnArgs), P(SvAcceptArgs)]
         L.sv_workspace_bytes.restype = ctypes.c_size_t
         L.sv_status_string.argtypes = [ctypes.c_int32]
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_last_error.argtypes = []
         L.sv_last_error.restype = ctypes.c_char_p
-        for f in ("sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step"):
+        for f in ("sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_commit_accepted"):
             getattr(L, f).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -143,6 +155,19 @@ def make_accept_args(target_logits, q_probs, temperature, u_accept, u_sample, ou
     return a
 
 
+def make_commit_args(k_new, v_new, k_cache, v_cache, prefix_len, prefix_len_out, feat_in=None, feat_out=None):
+    """sv_commit_args: k_new/v_new [B][T_max][Hkv][D], k_cache/v_cache [B][Hkv][L_max][D],
+    prefix_len / prefix_len_out int32 [B], optional feat_in / feat_out [B][T_max][F]."""
+    Hkv, D = int(k_new.shape[2]), int(k_new.shape[3])
+    L_max = int(k_cache.shape[2])
+    F = 0 if feat_in is None else int(feat_in.shape[2])
+    fdt = SV_F32 if feat_in is None else _dtype_code(feat_in)
+    a = SvCommitArgs(Hkv, D, L_max, _dtype_code(k_new), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                     _ptr(prefix_len), _ptr(prefix_len_out), F, fdt, _ptr(feat_in), _ptr(feat_out))
+    a._keep = (k_new, v_new, k_cache, v_cache, prefix_len, prefix_len_out, feat_in, feat_out)
+    return a
+
+
 def _check(code, where, raise_on_error):
     if code != SV_OK and raise_on_error:
         raise SvError(code, where)
@@ -172,6 +197,12 @@ def sv_verify_step(tree, attn, acc, anc, depth, tree_status, ws, stream=None, ra
     return _check(lib().sv_verify_step(ctypes.byref(tree), ctypes.byref(attn), ctypes.byref(acc), _ptr(anc),
                                        _ptr(depth), _ptr(tree_status), _ptr(ws), nbytes, _stream(stream)),
                   "sv_verify_step", raise_on_error)
+
+
+def sv_commit_accepted(tree, tree_status, out_nodes, out_count, commit, stream=None, raise_on_error=True):
+    return _check(lib().sv_commit_accepted(ctypes.byref(tree), _ptr(tree_status), _ptr(out_nodes), _ptr(out_count),
+                                           ctypes.byref(commit), _stream(stream)),
+                  "sv_commit_accepted", raise_on_error)
 
 
 def sv_workspace_bytes(tree, attn=None, acc=None):

@@ -94,6 +94,34 @@ sv_status check_accept(const sv_tree* t, const sv_accept_args* a) {
   return SV_OK;
 }
 
+sv_status check_commit(const sv_tree* t, const sv_commit_args* c) {
+  if (!c) { set_error("commit args are NULL"); return SV_E_NULL; }
+  if (c->dtype != SV_F32 && c->dtype != SV_BF16) { set_error("commit dtype %d", c->dtype); return SV_E_DTYPE; }
+  if (c->F > 0 && c->feat_dtype != SV_F32 && c->feat_dtype != SV_BF16) {
+    set_error("feature dtype %d", c->feat_dtype);
+    return SV_E_DTYPE;
+  }
+  const int es = c->dtype == SV_BF16 ? 2 : 4;
+  if (c->Hkv < 1 || c->D < 1 || c->L_max < 0 || c->F < 0) {
+    set_error("commit sizes Hkv=%d D=%d L_max=%d F=%d", c->Hkv, c->D, c->L_max, c->F);
+    return SV_E_SHAPE;
+  }
+  if ((c->D * es) % 16 != 0) { set_error("commit rows of %d bytes (need a multiple of 16)", c->D * es); return SV_E_UNSUPPORTED; }
+  if ((long)t->B * c->Hkv > 0x7FFFFFFFL || c->Hkv > 65535) { set_error("B*Hkv too large"); return SV_E_UNSUPPORTED; }
+  if (t->B > 0) {
+    if (!c->k_new || !c->v_new || !c->k_cache || !c->v_cache || !c->prefix_len || !c->prefix_len_out) {
+      set_error("commit k_new/v_new/k_cache/v_cache/prefix_len/prefix_len_out is NULL");
+      return SV_E_NULL;
+    }
+    if (c->F > 0 && (!c->feat_in || !c->feat_out)) { set_error("feat_in/feat_out is NULL"); return SV_E_NULL; }
+    if (c->prefix_len == c->prefix_len_out) { set_error("prefix_len_out must not alias prefix_len"); return SV_E_SHAPE; }
+    const void* ptrs[] = {c->k_new, c->v_new, c->k_cache, c->v_cache, c->feat_in, c->feat_out};
+    for (const void* q : ptrs)
+      if (q && !aligned(q, 16)) { set_error("commit tensors must be 16-byte aligned"); return SV_E_UNSUPPORTED; }
+  }
+  return SV_OK;
+}
+
 sv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return SV_OK;
   if (!ws) { set_error("workspace is NULL (need %zu bytes)", need); return SV_E_WORKSPACE; }
@@ -165,6 +193,19 @@ sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv
   return launch_accept(tree, tree_status, acc, cp, ws, s);
 }
 
+sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const int32_t* out_nodes,
+                             const int32_t* out_count, const sv_commit_args* c, void* stream) {
+  clear_error();
+  sv_status st = check_tree(tree, false);
+  if (st) return st;
+  if ((st = check_commit(tree, c))) return st;
+  if (tree->B > 0 && (!tree_status || !out_nodes || !out_count)) {
+    set_error("tree_status/out_nodes/out_count is NULL");
+    return SV_E_NULL;
+  }
+  return launch_commit(tree, tree_status, out_nodes, out_count, c, (hipStream_t)stream);
+}
+
 size_t sv_workspace_bytes(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc) {
   clear_error();
   // sizing reads only the scalar fields: pointers may be NULL here
@@ -206,6 +247,8 @@ const char* sv_status_string(sv_status s) {
     case SV_TREE_E_NONFINITE: return "tree: non-finite target logit";
     case SV_TREE_E_NOQ: return "tree: stochastic sequence without draft probabilities";
     case SV_TREE_E_SYNC: return "tree: cross-workgroup wait timed out";
+    case SV_TREE_E_CACHE: return "commit: no room in the cache";
+    case SV_TREE_E_PATH: return "commit: accepted path out of range";
     default: return "unknown status";
   }
 }

@@ -56,6 +56,10 @@ bool plan_accept(const sv_tree* t, const sv_accept_args* a, AcceptPlan* p);
 sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_args* a,
                         const AcceptPlan& p, void* ws, hipStream_t s);
 
+// ---------------------------------------------------------------- commit
+sv_status launch_commit(const sv_tree* t, int32_t* tree_status, const int32_t* out_nodes,
+                        const int32_t* out_count, const sv_commit_args* a, hipStream_t s);
+
 // ---------------------------------------------------------------- mask
 sv_status launch_mask(const sv_tree* t, uint64_t* anc, int32_t* depth, int32_t* tree_status,
                       hipStream_t s);

@@ -7,8 +7,9 @@ the current torch stream.  Nothing here computes any part of the verification.
 """
 import numpy as np
 
-from . import (SV_SIB_IID, SV_SIB_WITHOUT_REPLACEMENT, make_accept_args, make_attn_args, make_tree,
-               sv_spec_accept, sv_tree_attn, sv_tree_mask_build, sv_verify_step, sv_workspace_bytes)
+from . import (SV_SIB_IID, SV_SIB_WITHOUT_REPLACEMENT, make_accept_args, make_attn_args, make_commit_args,
+               make_tree, sv_commit_accepted, sv_spec_accept, sv_tree_attn, sv_tree_mask_build, sv_verify_step,
+               sv_workspace_bytes)
 
 
 def to_device(arr, dtype, device):
@@ -92,6 +93,21 @@ class DeviceProblem:
     def verify_step(self, stream=None):
         return sv_verify_step(self.tree, self.attn, self.acc, self.anc, self.depth, self.status,
                               self.ws, stream)
+
+    def commit_args(self, feat_in=None):
+        """Commit arguments writing into this problem's caches; new lengths go to
+        ``self.prefix_len_out`` and features (optional [B][T_max][F] tensor) to
+        ``self.feat_out``."""
+        import torch
+        self.prefix_len_out = torch.full_like(self.prefix_len, -7)
+        self.feat_in = feat_in
+        self.feat_out = None if feat_in is None else torch.full_like(feat_in, 7.0)
+        self.commit = make_commit_args(self.k_new, self.v_new, self.k_cache, self.v_cache, self.prefix_len,
+                                       self.prefix_len_out, self.feat_in, self.feat_out)
+        return self.commit
+
+    def commit_accepted(self, stream=None):
+        return sv_commit_accepted(self.tree, self.status, self.out_nodes, self.out_count, self.commit, stream)
 
     # ---- results on the host
     def mask_results(self):

@@ -70,7 +70,9 @@ enum {
   SV_TREE_E_TOKEN = 4,     /* some tokens[b][i], i < T_b, outside [0, V)              */
   SV_TREE_E_NONFINITE = 5, /* a NaN or +-Inf in the logits row of a node the walk visits */
   SV_TREE_E_NOQ = 6,       /* temperature[b] > 0 but q_probs is NULL                  */
-  SV_TREE_E_SYNC = 7       /* internal: a cross-workgroup wait timed out              */
+  SV_TREE_E_SYNC = 7,      /* internal: a cross-workgroup wait timed out              */
+  SV_TREE_E_CACHE = 8,     /* commit: L_b + out_count[b] exceeds L_max (or L_b < 0)   */
+  SV_TREE_E_PATH = 9       /* commit: out_count[b] > T_b or a path entry outside [1, T_b) */
 };
 
 /* Element types. */
@@ -182,6 +184,44 @@ sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_acc
 /* One verification step: sv_tree_mask_build, then sv_tree_attn, then
  * sv_spec_accept, in stream order, sharing one workspace of at least
  * sv_workspace_bytes(tree, attn, acc) bytes. */
+/* Commit of the accepted path: cache growth and drafter features. */
+typedef struct {
+  int32_t Hkv, D;           /* KV heads and head dim of the caches (any D with D*size % 16 == 0) */
+  int32_t L_max;            /* capacity of the caches' length axis                      */
+  int32_t dtype;            /* SV_F32 or SV_BF16 for k_new, v_new and the caches        */
+  const void* k_new;        /* [B][T_max][Hkv][D] keys of the verified positions        */
+  const void* v_new;        /* [B][T_max][Hkv][D] values of the verified positions      */
+  void* k_cache;            /* [B][Hkv][L_max][D]: rows [L_b, L_b + c) written          */
+  void* v_cache;            /* [B][Hkv][L_max][D]: rows [L_b, L_b + c) written          */
+  const int32_t* prefix_len;/* [B] L_b before the commit (read)                         */
+  int32_t* prefix_len_out;  /* [B] L_b + c (L_b when nothing is committed); must not
+                               alias prefix_len                                          */
+  int32_t F;                /* feature width per position; 0 = no features              */
+  int32_t feat_dtype;       /* SV_F32 or SV_BF16 for feat_in / feat_out                 */
+  const void* feat_in;      /* [B][T_max][F] features of the verified positions         */
+  void* feat_out;           /* [B][T_max][F]: rows [0, c) = committed positions' rows,
+                               other rows zero                                           */
+} sv_commit_args;
+
+/* Commit of the accepted path ([EAGLE article] sec. 1.3 "Verification": the
+ * accepted tokens and their features are kept and drafting continues from
+ * them; [Spec-decoding lesson] "Concept": the accepted tokens extend the
+ * output and the correction / bonus token is the next position to run).
+ * For every sequence b with tree_status[b] == 0 and c = out_count[b] >= 1,
+ * the verified positions [0 (root), out_nodes[b][0], ..., out_nodes[b][c-2]]
+ * have their K and V rows (every KV head) copied, bit for bit, to cache rows
+ * L_b .. L_b + c - 1, prefix_len_out[b] = L_b + c, and their feature rows to
+ * feat_out rows 0 .. c-1.  The emitted token out_tokens[b][c-1] is the next
+ * root: its rows come from the next forward pass.
+ *   tree: B, T_max, num_nodes (parent and tokens are not read).
+ *   tree_status [B] (in/out): sequences not OK are left alone; SV_TREE_E_CACHE
+ *   or SV_TREE_E_PATH is written when a commit does not fit or the path is out
+ *   of range (then nothing of that sequence is written, prefix_len_out = L_b).
+ *   out_nodes / out_count: as written by sv_spec_accept.
+ * Needs no workspace.  Tensors must be 16-byte aligned. */
+sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const int32_t* out_nodes,
+                             const int32_t* out_count, const sv_commit_args* c, void* stream);
+
 sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
                          uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws,
                          size_t ws_bytes, void* stream);
