@@ -159,6 +159,26 @@ def summarize_counters(fetch_csv, write_csv):
     print(json.dumps(out, indent=1))
 
 
+def time_commit(dev, inst, res, n, stream):
+    """sv_commit_accepted on the step's accept results, into destination caches
+    of L_max = prefix + T_max; returns (ms per launch, bytes moved)."""
+    import torch
+    import eagle_tree_verification_attn_amd as sv
+    dst_shape = (inst.B, inst.Hkv, int(inst.prefix_len.max()) + inst.T_max, inst.D)
+    kd = torch.empty(dst_shape, dtype=dev.k_cache.dtype, device=dev.k_cache.device)
+    vd = torch.empty_like(kd)
+    plen_out = torch.empty_like(dev.prefix_len)
+    args = sv.make_commit_args(dev.k_new, dev.v_new, kd, vd, dev.prefix_len, plen_out)
+    status = dev.status.clone()
+    fn = lambda: sv.sv_commit_accepted(dev.tree, status, dev.out_nodes, dev.out_count, args, stream)
+    for _ in range(3):          # the first launch loads the kernel
+        fn()
+    ms = time_launches(fn, n, stream)
+    s = 2 if inst.dtype == "bf16" else 4
+    rows = int(res["out_count"][res["status"] == 0].sum())
+    return ms, float(2 * 2 * rows * inst.Hkv * inst.D * s)     # K and V rows, read and written
+
+
 def cpu_baseline(inst, seconds):
     """The oracle on a bounded sample: whole sequences (attention for all heads,
     target softmax and walk), scaled to steps/s of the full batch."""
@@ -262,6 +282,9 @@ def main():
     attn_ms = time_launches(dev.tree_attn, n, stream)
     acc_ms = time_launches(dev.spec_accept, n, stream)
     res = dev.accept_results()
+    # the commit of the accepted path (not part of the step): into caches with
+    # room after the prefix, so the step's own caches stay as they are
+    commit_ms, commit_bytes = time_commit(dev, inst, res, n, stream)
     flops, attn_bytes = algorithmic_work(inst)
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
@@ -299,6 +322,8 @@ def main():
         "cpu_baseline": cpu,
         "kernels_ms": {"tree_mask_build": round(mask_ms, 5), "tree_attn": round(attn_ms, 5),
                        "spec_accept": round(acc_ms, 5)},
+        "commit_accepted": {"ms": round(commit_ms, 5), "bytes": commit_bytes,
+                            "note": "after the step, not part of it"},
         "hbm_roofline": {"tree_attn_verify": {"algorithmic_bytes": attn_bytes,
                                               "GB_s": round(attn_gbs, 1),
                                               "frac": round(attn_gbs / HBM_PEAK_GBS, 4)},

@@ -12,6 +12,10 @@
 // new length and any status.  Every workgroup of a sequence takes the same
 // decision from the same inputs, so none waits for another.  The work is a
 // small gather: about 2 c rows of D elements per head and sequence.
+// The bookkeeper's status write may land before another workgroup of the same
+// sequence reads that word.  It only ever turns OK into an error, and it does
+// so exactly when the checks below fail, so either value read leads that
+// workgroup to write nothing.
 #include "sv_internal.h"
 
 namespace sv {
@@ -38,15 +42,28 @@ struct CommitParams {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Copy of nbytes between 16-byte aligned rows, or in 2-byte units otherwise
-// (feature rows need not be multiples of 16 bytes).
-__device__ inline void copy_row(unsigned char* dst, const unsigned char* src, int nbytes, int t, int nt) {
+// Copies rows n of src (row pitch src_pitch) to rows row0 + i of dst (pitch
+// dst_pitch), where pos_s[i] = n, i < rows.  Every (row, unit) pair goes to its
+// own thread, so all rows are in flight at once.  Units are 16 bytes when the
+// row length allows it, else 2 bytes (feature rows may have any width).
+__device__ inline void gather_rows(unsigned char* dst, size_t dst_pitch, int row0, const unsigned char* src,
+                                   size_t src_pitch, const int* pos_s, int rows, int nbytes, int tid) {
   if ((nbytes & 15) == 0) {
-    for (int i = t * 16; i < nbytes; i += nt * 16)
-      *reinterpret_cast<u32x4*>(dst + i) = *reinterpret_cast<const u32x4*>(src + i);
+    const int per_row = nbytes >> 4;
+    for (int u = tid; u < rows * per_row; u += kCommitThreads) {
+      const int i = u / per_row;
+      const int j = (u - i * per_row) << 4;
+      *reinterpret_cast<u32x4*>(dst + (size_t)(row0 + i) * dst_pitch + j) =
+          *reinterpret_cast<const u32x4*>(src + (size_t)pos_s[i] * src_pitch + j);
+    }
   } else {
-    for (int i = t * 2; i < nbytes; i += nt * 2)
-      *reinterpret_cast<uint16_t*>(dst + i) = *reinterpret_cast<const uint16_t*>(src + i);
+    const int per_row = nbytes >> 1;
+    for (int u = tid; u < rows * per_row; u += kCommitThreads) {
+      const int i = u / per_row;
+      const int j = (u - i * per_row) << 1;
+      *reinterpret_cast<uint16_t*>(dst + (size_t)(row0 + i) * dst_pitch + j) =
+          *reinterpret_cast<const uint16_t*>(src + (size_t)pos_s[i] * src_pitch + j);
+    }
   }
 }
 
@@ -89,12 +106,21 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(CommitParams p) {
     if (!go) return;
     const int h = y;
     const size_t new_row = (size_t)p.Hkv * p.row_bytes;                       // between positions
-    const size_t cache_head = ((size_t)b * p.Hkv + h) * p.L_max * p.row_bytes;
-    for (int i = 0; i < c; ++i) {
-      const size_t src = ((size_t)b * p.T_max + pos_s[i]) * new_row + (size_t)h * p.row_bytes;
-      const size_t dst = cache_head + (size_t)(L + i) * p.row_bytes;
-      copy_row(p.k_cache + dst, p.k_new + src, p.row_bytes, tid, kCommitThreads);
-      copy_row(p.v_cache + dst, p.v_new + src, p.row_bytes, tid, kCommitThreads);
+    const size_t src = (size_t)b * p.T_max * new_row + (size_t)h * p.row_bytes;
+    const size_t dst = ((size_t)b * p.Hkv + h) * p.L_max * p.row_bytes;
+    // K and V in one pass: units [0, c*per_row) are K, the rest V
+    const int per_row = p.row_bytes >> 4;
+    const int units = c * per_row;
+    for (int u = tid; u < 2 * units; u += kCommitThreads) {
+      const bool is_v = u >= units;
+      const int r = is_v ? u - units : u;
+      const int i = r / per_row;
+      const int j = (r - i * per_row) << 4;
+      const uint64_t from = reinterpret_cast<uint64_t>(is_v ? p.v_new : p.k_new) + src +
+                            (size_t)pos_s[i] * new_row + j;
+      const uint64_t to = reinterpret_cast<uint64_t>(is_v ? p.v_cache : p.k_cache) + dst +
+                          (size_t)(L + i) * p.row_bytes + j;
+      *reinterpret_cast<u32x4*>(to) = *reinterpret_cast<const u32x4*>(from);
     }
     return;
   }
@@ -102,9 +128,8 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(CommitParams p) {
   if (p.feat_bytes > 0) {
     const size_t fb = (size_t)p.feat_bytes;
     const int n_rows = go ? c : 0;
-    for (int i = 0; i < n_rows; ++i)
-      copy_row(p.feat_out + ((size_t)b * p.T_max + i) * fb, p.feat_in + ((size_t)b * p.T_max + pos_s[i]) * fb,
-               p.feat_bytes, tid, kCommitThreads);
+    const size_t seq = (size_t)b * p.T_max * fb;
+    gather_rows(p.feat_out + seq, fb, 0, p.feat_in + seq, fb, pos_s, n_rows, p.feat_bytes, tid);
     unsigned char* rest = p.feat_out + ((size_t)b * p.T_max + n_rows) * fb;
     const size_t rest_bytes = (size_t)(p.T_max - n_rows) * fb;
     for (size_t i = (size_t)tid * 2; i < rest_bytes; i += kCommitThreads * 2)

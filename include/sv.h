@@ -184,6 +184,10 @@ sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_acc
 /* One verification step: sv_tree_mask_build, then sv_tree_attn, then
  * sv_spec_accept, in stream order, sharing one workspace of at least
  * sv_workspace_bytes(tree, attn, acc) bytes. */
+sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
+                         uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* Commit of the accepted path: cache growth and drafter features. */
 typedef struct {
   int32_t Hkv, D;           /* KV heads and head dim of the caches (any D with D*size % 16 == 0) */
@@ -221,10 +225,6 @@ typedef struct {
  * Needs no workspace.  Tensors must be 16-byte aligned. */
 sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const int32_t* out_nodes,
                              const int32_t* out_count, const sv_commit_args* c, void* stream);
-
-sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
-                         uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws,
-                         size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by sv_tree_attn (attn != NULL), sv_spec_accept
  * (acc != NULL) or both (the maximum).  Host only; reads only the scalar
