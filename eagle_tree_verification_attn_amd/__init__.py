@@ -20,12 +20,13 @@ LIB_PATH = os.path.join(_HERE, "libsv.so")
 SV_OK, SV_E_NULL, SV_E_SHAPE, SV_E_DTYPE, SV_E_WORKSPACE, SV_E_HIP, SV_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 SV_TREE_OK, SV_TREE_E_ROOT, SV_TREE_E_PARENT, SV_TREE_E_COUNT = 0, 1, 2, 3
 SV_TREE_E_TOKEN, SV_TREE_E_NONFINITE, SV_TREE_E_NOQ, SV_TREE_E_SYNC = 4, 5, 6, 7
-SV_TREE_E_CACHE, SV_TREE_E_PATH = 8, 9
+SV_TREE_E_CACHE, SV_TREE_E_PATH, SV_TREE_E_PROB = 8, 9, 10
 SV_F32, SV_BF16 = 0, 1
 SV_SIB_WITHOUT_REPLACEMENT, SV_SIB_IID = 0, 1
 
 EXPORTS = ["sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step",
-           "sv_commit_accepted", "sv_workspace_bytes", "sv_status_string", "sv_last_error"]
+           "sv_commit_accepted", "sv_workspace_bytes", "sv_status_string", "sv_last_error",
+           "sv_eagle2_state_bytes", "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish"]
 
 
 class SvTree(ctypes.Structure):
@@ -48,6 +49,11 @@ class SvAcceptArgs(ctypes.Structure):
                 ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p),
                 ("out_tokens", ctypes.c_void_p), ("out_nodes", ctypes.c_void_p),
                 ("out_count", ctypes.c_void_p), ("out_passes", ctypes.c_void_p)]
+
+
+class SvEagle2Cfg(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("V", ctypes.c_int32), ("k", ctypes.c_int32), ("depth", ctypes.c_int32),
+                ("m", ctypes.c_int32)]
 
 
 class SvCommitArgs(ctypes.Structure):
@@ -87,13 +93,23 @@ def lib():
                                      ctypes.c_void_p]
         L.sv_commit_accepted.argtypes = [P(SvTree), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          P(SvCommitArgs), ctypes.c_void_p]
+        L.sv_eagle2_state_bytes.argtypes = [P(SvEagle2Cfg)]
+        L.sv_eagle2_state_bytes.restype = ctypes.c_size_t
+        L.sv_eagle2_begin.argtypes = [P(SvEagle2Cfg), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+        L.sv_eagle2_expand.argtypes = [P(SvEagle2Cfg), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.sv_eagle2_finish.argtypes = [P(SvEagle2Cfg), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
         L.sv_workspace_bytes.argtypes = [P(SvTree), P(SvAttnArgs), P(SvAcceptArgs)]
         L.sv_workspace_bytes.restype = ctypes.c_size_t
         L.sv_status_string.argtypes = [ctypes.c_int32]
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_last_error.argtypes = []
         L.sv_last_error.restype = ctypes.c_char_p
-        for f in ("sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_commit_accepted"):
+        for f in ("sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_commit_accepted",
+                  "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish"):
             getattr(L, f).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -203,6 +219,31 @@ def sv_commit_accepted(tree, tree_status, out_nodes, out_count, commit, stream=N
     return _check(lib().sv_commit_accepted(ctypes.byref(tree), _ptr(tree_status), _ptr(out_nodes), _ptr(out_count),
                                            ctypes.byref(commit), _stream(stream)),
                   "sv_commit_accepted", raise_on_error)
+
+
+def sv_eagle2_state_bytes(cfg):
+    return int(lib().sv_eagle2_state_bytes(ctypes.byref(cfg)))
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def sv_eagle2_begin(cfg, state, root_tokens, stream=None, raise_on_error=True):
+    return _check(lib().sv_eagle2_begin(ctypes.byref(cfg), _ptr(state), _nbytes(state), _ptr(root_tokens),
+                                        _stream(stream)), "sv_eagle2_begin", raise_on_error)
+
+
+def sv_eagle2_expand(cfg, state, step, q, frontier=None, frontier_tokens=None, stream=None, raise_on_error=True):
+    return _check(lib().sv_eagle2_expand(ctypes.byref(cfg), _ptr(state), _nbytes(state), int(step), _ptr(q),
+                                         _ptr(frontier), _ptr(frontier_tokens), _stream(stream)),
+                  "sv_eagle2_expand", raise_on_error)
+
+
+def sv_eagle2_finish(cfg, state, parent, tokens, num_nodes, q_row, status, stream=None, raise_on_error=True):
+    return _check(lib().sv_eagle2_finish(ctypes.byref(cfg), _ptr(state), _nbytes(state), _ptr(parent), _ptr(tokens),
+                                         _ptr(num_nodes), _ptr(q_row), _ptr(status), _stream(stream)),
+                  "sv_eagle2_finish", raise_on_error)
 
 
 def sv_workspace_bytes(tree, attn=None, acc=None):

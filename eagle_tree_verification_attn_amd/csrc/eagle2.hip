@@ -1,0 +1,426 @@
+// EAGLE-2 draft-tree builder ([EAGLE article] sec. 2.3 "Context-aware draft
+// tree": node value = product of draft confidences along the path; expansion
+// of the k best nodes of the newest layer; rerank of the m best nodes of the
+// whole tree, equal values to the shallower node; flattening for
+// verification).
+//
+// Three kernels:
+//   k_row_topk     one workgroup per (sequence, frontier row, vocabulary
+//                  chunk): streams the chunk of the drafter's probability row
+//                  once, keeps each thread's k best (probability, token) keys
+//                  in registers, merges them across the block and checks the
+//                  range.  This is the HBM-bound part.
+//   k_expand       one workgroup per sequence: merges the chunks' keys of each
+//                  frontier row, appends the children (value = parent value x
+//                  probability, one float32 multiply) and ranks the new layer
+//                  to pick the next frontier.
+//   k_finish       one workgroup per sequence: ranks every draft node, keeps
+//                  the m best and assigns flattened positions depth by depth.
+//
+// A (probability, token) pair is one 64-bit key: the probability's bits (it is
+// in [0, 1], so its bit pattern orders like its value once -0 is made +0) above
+// the complement of the token.  The larger key is the higher probability, then
+// the lower token; 0 is below every real key.
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int kTopkThreads = 256;
+constexpr int kE2MaxK = 16;
+constexpr int kE2Threads = 256;
+constexpr int kFinishThreads = 1024;
+
+struct E2Params {
+  int B, V, k, depth, m, nsplit, chunk, nmax;
+  int32_t* seq;        // [B][8]: n_nodes, layer_begin, nfront, status
+  int32_t* front;      // [B][16]
+  int32_t* parent;     // [B][nmax]
+  int32_t* token;      // [B][nmax]
+  int32_t* depthv;     // [B][nmax]
+  int32_t* rank;       // [B][nmax] rank among siblings
+  int32_t* qrow;       // [B][nmax]
+  float* value;        // [B][nmax]
+  uint64_t* cand;      // [B][k][nsplit][k]
+  int32_t* cand_bad;   // [B][k][nsplit]
+};
+
+enum { kSeqN = 0, kSeqLayer = 1, kSeqFront = 2, kSeqStatus = 3 };
+
+E2Layout eagle2_layout(const sv_eagle2_cfg* c) {
+  E2Layout L{};
+  L.nmax = 1 + c->k + (c->depth - 1) * c->k * c->k;
+  L.nsplit = (c->V + 8191) / 8192;
+  if (L.nsplit > 16) L.nsplit = 16;
+  if (L.nsplit < 1) L.nsplit = 1;
+  L.chunk = (c->V + L.nsplit - 1) / L.nsplit;
+  L.chunk = (L.chunk + 3) / 4 * 4;
+  size_t o = 0;
+  const size_t B = (size_t)c->B, N = (size_t)L.nmax, k = (size_t)c->k;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, kWsAlign); return at; };
+  L.off_seq = take(B * 8 * 4);
+  L.off_front = take(B * 16 * 4);
+  L.off_parent = take(B * N * 4);
+  L.off_token = take(B * N * 4);
+  L.off_depth = take(B * N * 4);
+  L.off_rank = take(B * N * 4);
+  L.off_qrow = take(B * N * 4);
+  L.off_value = take(B * N * 4);
+  L.off_cand = take(B * k * (size_t)L.nsplit * k * 8);
+  L.off_bad = take(B * k * (size_t)L.nsplit * 4);
+  L.bytes = o;
+  return L;
+}
+
+static E2Params make_params(const sv_eagle2_cfg* c, const E2Layout& L, void* state) {
+  unsigned char* base = static_cast<unsigned char*>(state);
+  E2Params p{};
+  p.B = c->B; p.V = c->V; p.k = c->k; p.depth = c->depth; p.m = c->m;
+  p.nsplit = L.nsplit; p.chunk = L.chunk; p.nmax = L.nmax;
+  p.seq = reinterpret_cast<int32_t*>(base + L.off_seq);
+  p.front = reinterpret_cast<int32_t*>(base + L.off_front);
+  p.parent = reinterpret_cast<int32_t*>(base + L.off_parent);
+  p.token = reinterpret_cast<int32_t*>(base + L.off_token);
+  p.depthv = reinterpret_cast<int32_t*>(base + L.off_depth);
+  p.rank = reinterpret_cast<int32_t*>(base + L.off_rank);
+  p.qrow = reinterpret_cast<int32_t*>(base + L.off_qrow);
+  p.value = reinterpret_cast<float*>(base + L.off_value);
+  p.cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
+  p.cand_bad = reinterpret_cast<int32_t*>(base + L.off_bad);
+  return p;
+}
+
+__device__ inline uint64_t prob_key(float v, int tok) {
+  const float z = v + 0.0f;   // -0 -> +0
+  return ((uint64_t)__float_as_uint(z) << 32) | (uint64_t)(~(uint32_t)tok);
+}
+__device__ inline float key_prob(uint64_t key) { return __uint_as_float((uint32_t)(key >> 32)); }
+__device__ inline int key_token(uint64_t key) { return (int)(~(uint32_t)key); }
+
+// Inserts key x into the descending list t[0..kE2MaxK) (entries past k are
+// don't-care); the caller has checked that x beats t[k - 1].
+__device__ inline void list_insert(uint64_t (&t)[kE2MaxK], uint64_t x) {
+#pragma unroll
+  for (int p = kE2MaxK - 1; p > 0; --p) {
+    const bool shift = x > t[p - 1];
+    const bool here = !shift && x > t[p];
+    t[p] = shift ? t[p - 1] : (here ? x : t[p]);
+  }
+  if (x > t[0]) t[0] = x;
+}
+
+__device__ inline uint64_t list_at(const uint64_t (&t)[kE2MaxK], int i) {
+  uint64_t r = 0;
+#pragma unroll
+  for (int p = 0; p < kE2MaxK; ++p) r = (p == i) ? t[p] : r;
+  return r;
+}
+
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- begin
+__global__ void k_e2_begin(E2Params p, const int32_t* root_tokens) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= p.B) return;
+  int32_t* s = p.seq + (size_t)b * 8;
+  s[kSeqN] = 1;
+  s[kSeqLayer] = 0;
+  s[kSeqFront] = 1;
+  s[kSeqStatus] = SV_TREE_OK;
+  for (int j = 0; j < 16; ++j) p.front[(size_t)b * 16 + j] = j == 0 ? 0 : -1;
+  const size_t n0 = (size_t)b * p.nmax;
+  p.parent[n0] = -1;
+  p.token[n0] = root_tokens[b];
+  p.depthv[n0] = 0;
+  p.rank[n0] = 0;
+  p.qrow[n0] = -1;
+  p.value[n0] = 1.0f;
+}
+
+// ---------------------------------------------------------------- row top-k
+// grid: B * k * nsplit workgroups; workgroup (b, j, c) reads chunk c of row j.
+__global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const float* q) {
+  const int c = blockIdx.x % p.nsplit;
+  const int j = (blockIdx.x / p.nsplit) % p.k;
+  const int b = blockIdx.x / (p.nsplit * p.k);
+  const int tid = threadIdx.x;
+  const int32_t* s = p.seq + (size_t)b * 8;
+  if (s[kSeqStatus] != SV_TREE_OK || j >= s[kSeqFront]) return;
+  const int lo = c * p.chunk;
+  const int hi = min(p.V, lo + p.chunk);
+  const float* row = q + ((size_t)b * p.k + j) * p.V;
+  uint64_t t[kE2MaxK];
+#pragma unroll
+  for (int i = 0; i < kE2MaxK; ++i) t[i] = 0;
+  uint64_t thr = 0;       // t[k - 1]
+  bool bad = false;
+  auto consider = [&](float v, int i) {
+    bad |= !(v >= 0.0f && v <= 1.0f);
+    const uint64_t key = prob_key(v, i);
+    if (key > thr) {
+      list_insert(t, key);
+      thr = list_at(t, p.k - 1);
+    }
+  };
+  if ((p.V & 3) == 0 && (lo & 3) == 0) {
+    const float4* r4 = reinterpret_cast<const float4*>(row + lo);
+    const int n4 = (hi - lo) >> 2;
+    int i = tid;
+    for (; i + 3 * kTopkThreads < n4; i += 4 * kTopkThreads) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = r4[i + u * kTopkThreads];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = lo + 4 * (i + u * kTopkThreads);
+        consider(v[u].x, e);
+        consider(v[u].y, e + 1);
+        consider(v[u].z, e + 2);
+        consider(v[u].w, e + 3);
+      }
+    }
+    for (; i < n4; i += kTopkThreads) {
+      const float4 v = r4[i];
+      const int e = lo + 4 * i;
+      consider(v.x, e);
+      consider(v.y, e + 1);
+      consider(v.z, e + 2);
+      consider(v.w, e + 3);
+    }
+    for (int e = lo + 4 * n4 + tid; e < hi; e += kTopkThreads) consider(row[e], e);
+  } else {
+    for (int e = lo + tid; e < hi; e += kTopkThreads) consider(row[e], e);
+  }
+  // block merge: k rounds, each taking the best head among the threads
+  __shared__ uint64_t wmax[kTopkThreads / 64];
+  __shared__ int bad_s;
+  if (tid == 0) bad_s = 0;
+  __syncthreads();
+  if (bad) bad_s = 1;
+  uint64_t* out = p.cand + (((size_t)b * p.k + j) * p.nsplit + c) * p.k;
+  for (int r = 0; r < p.k; ++r) {
+    const uint64_t w = wave_max_u64(t[0]);
+    if ((tid & 63) == 0) wmax[tid >> 6] = w;
+    __syncthreads();
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkThreads / 64; ++i) best = wmax[i] > best ? wmax[i] : best;
+    __syncthreads();
+    if (tid == 0) out[r] = best;
+    if (best != 0 && t[0] == best) {   // keys are distinct (tokens differ): one owner pops
+#pragma unroll
+      for (int i = 0; i < kE2MaxK - 1; ++i) t[i] = t[i + 1];
+      t[kE2MaxK - 1] = 0;
+    }
+  }
+  if (tid == 0) p.cand_bad[((size_t)b * p.k + j) * p.nsplit + c] = bad_s;
+}
+
+// ---------------------------------------------------------------- expand
+__global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int32_t* frontier_out,
+                                                       int32_t* frontier_tokens) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  int32_t* s = p.seq + (size_t)b * 8;
+  const size_t nb = (size_t)b * p.nmax;
+  const int k = p.k;
+  __shared__ uint64_t best_s[kE2MaxK][kE2MaxK];   // per frontier row, its k best keys
+  __shared__ float val_s[kE2MaxK * kE2MaxK];     // the new layer's values
+  __shared__ int bad_s;
+  const int status = s[kSeqStatus];
+  const int F = s[kSeqFront];
+  const int n0 = s[kSeqN];
+  if (tid == 0) bad_s = 0;
+  __syncthreads();
+  bool ok = status == SV_TREE_OK;
+  if (ok) {
+    for (int i = tid; i < F * p.nsplit; i += kE2Threads)
+      if (p.cand_bad[((size_t)b * k + i / p.nsplit) * p.nsplit + i % p.nsplit]) bad_s = 1;
+  }
+  __syncthreads();
+  if (ok && bad_s) {
+    ok = false;
+    if (tid == 0) s[kSeqStatus] = SV_TREE_E_PROB;
+  }
+  // more steps than the state was sized for: the node arrays are full
+  if (ok && n0 + F * k > p.nmax) {
+    ok = false;
+    if (tid == 0) s[kSeqStatus] = SV_TREE_E_COUNT;
+  }
+  if (ok) {
+    // merge: candidate e of row j ranks by the number of row-j candidates above it
+    const int C = p.nsplit * k;
+    for (int i = tid; i < F * C; i += kE2Threads) {
+      const int j = i / C;
+      const uint64_t* cj = p.cand + (size_t)(b * k + j) * C;
+      const uint64_t x = cj[i % C];
+      int r = 0;
+      for (int e = 0; e < C; ++e) r += cj[e] > x;
+      if (x != 0 && r < k) best_s[j][r] = x;
+    }
+    __syncthreads();
+    // children of frontier entry j: ids n0 + j k + r
+    for (int i = tid; i < F * k; i += kE2Threads) {
+      const int j = i / k, r = i % k;
+      const int par = p.front[(size_t)b * 16 + j];
+      const uint64_t key = best_s[j][r];
+      const float v = __fmul_rn(p.value[nb + par], key_prob(key));
+      const size_t id = nb + n0 + i;
+      p.parent[id] = par;
+      p.token[id] = key_token(key);
+      p.depthv[id] = p.depthv[nb + par] + 1;
+      p.rank[id] = r;
+      p.qrow[id] = -1;
+      p.value[id] = v;
+      val_s[i] = v;
+    }
+    for (int j = tid; j < F; j += kE2Threads) p.qrow[nb + p.front[(size_t)b * 16 + j]] = step * k + j;
+    __syncthreads();
+    // next frontier: the k best of the new layer (value descending, then id)
+    const int Lc = F * k;
+    if (tid < 16) p.front[(size_t)b * 16 + tid] = -1;
+    __syncthreads();
+    for (int i = tid; i < Lc; i += kE2Threads) {
+      const float v = val_s[i];
+      int r = 0;
+      for (int e = 0; e < Lc; ++e) r += (val_s[e] > v) || (val_s[e] == v && e < i);
+      if (r < k) p.front[(size_t)b * 16 + r] = n0 + i;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      s[kSeqLayer] = n0;
+      s[kSeqN] = n0 + Lc;
+      s[kSeqFront] = Lc < k ? Lc : k;
+    }
+  }
+  __syncthreads();
+  if (tid < k) {
+    const int id = ok ? p.front[(size_t)b * 16 + tid] : -1;
+    if (frontier_out) frontier_out[(size_t)b * k + tid] = id;
+    if (frontier_tokens) frontier_tokens[(size_t)b * k + tid] = id >= 0 ? p.token[nb + id] : -1;
+  }
+}
+
+// ---------------------------------------------------------------- finish
+__global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* parent_out, int32_t* tokens_out,
+                                                           int32_t* num_nodes, int32_t* q_row_out,
+                                                           int32_t* status_out) {
+  constexpr int kMaxNodes = 2048;
+  __shared__ float val_s[kMaxNodes];
+  __shared__ int dep_s[kMaxNodes];
+  __shared__ int pos_s[kMaxNodes];      // flattened position, -1 if not kept
+  __shared__ int key_s[kMaxNodes];      // per depth pass: parent position * 16 + rank
+  __shared__ int cnt_s;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t* s = p.seq + (size_t)b * 8;
+  const size_t nb = (size_t)b * p.nmax;
+  const int T = p.m + 1;
+  int status = s[kSeqStatus];
+  const int N = s[kSeqN];
+  if (status == SV_TREE_OK && (N - 1 < p.m || N > p.nmax)) status = SV_TREE_E_COUNT;   // too few steps ran
+  if (tid == 0) status_out[b] = status;
+  const bool ok = status == SV_TREE_OK;
+  if (!ok) {
+    for (int i = tid; i < T; i += kFinishThreads) {
+      parent_out[(size_t)b * T + i] = -1;
+      tokens_out[(size_t)b * T + i] = -1;
+      q_row_out[(size_t)b * T + i] = -1;
+    }
+    if (tid == 0) num_nodes[b] = 0;
+    return;
+  }
+  for (int i = tid; i < N; i += kFinishThreads) {
+    val_s[i] = p.value[nb + i];
+    dep_s[i] = p.depthv[nb + i];
+    pos_s[i] = -1;
+  }
+  __syncthreads();
+  // keep the m best draft nodes: value descending, depth ascending, id ascending
+  for (int i = 1 + tid; i < N; i += kFinishThreads) {
+    const float v = val_s[i];
+    const int d = dep_s[i];
+    int r = 0;
+    for (int e = 1; e < N; ++e) {
+      const float ve = val_s[e];
+      r += (ve > v) || (ve == v && (dep_s[e] < d || (dep_s[e] == d && e < i)));
+    }
+    pos_s[i] = r < p.m ? 0 : -1;      // 0 marks kept; the position comes below
+  }
+  if (tid == 0) pos_s[0] = 0;
+  __syncthreads();
+  // positions depth by depth: after the earlier depths, ordered by parent
+  // position then sibling rank
+  int base = 1;
+  for (int d = 1; d <= p.depth; ++d) {
+    for (int i = 1 + tid; i < N; i += kFinishThreads)
+      key_s[i] = (dep_s[i] == d && pos_s[i] >= 0) ? pos_s[p.parent[nb + i]] * 16 + p.rank[nb + i] : -1;
+    if (tid == 0) cnt_s = 0;
+    __syncthreads();
+    for (int i = 1 + tid; i < N; i += kFinishThreads) {
+      const int key = key_s[i];
+      if (key < 0) continue;
+      int r = 0;
+      for (int e = 1; e < N; ++e) r += key_s[e] >= 0 && key_s[e] < key;
+      pos_s[i] = base + r;
+      atomicAdd(&cnt_s, 1);
+    }
+    __syncthreads();
+    base += cnt_s;
+    __syncthreads();
+  }
+  for (int i = tid; i < N; i += kFinishThreads) {
+    const int ps = pos_s[i];
+    if (ps < 0 || ps >= T) continue;
+    parent_out[(size_t)b * T + ps] = i == 0 ? -1 : pos_s[p.parent[nb + i]];
+    tokens_out[(size_t)b * T + ps] = p.token[nb + i];
+    q_row_out[(size_t)b * T + ps] = p.qrow[nb + i];
+  }
+  if (tid == 0) num_nodes[b] = T;
+}
+
+// ---------------------------------------------------------------- launchers
+sv_status launch_eagle2_begin(const sv_eagle2_cfg* c, void* state, const int32_t* root_tokens, hipStream_t s) {
+  const E2Layout L = eagle2_layout(c);
+  const E2Params p = make_params(c, L, state);
+  if (c->B == 0) return SV_OK;
+  hipLaunchKernelGGL(k_e2_begin, dim3((c->B + 255) / 256), dim3(256), 0, s, p, root_tokens);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) { set_error("eagle2 begin launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  return SV_OK;
+}
+
+sv_status launch_eagle2_expand(const sv_eagle2_cfg* c, void* state, int step, const float* q, int32_t* frontier,
+                               int32_t* frontier_tokens, hipStream_t s) {
+  const E2Layout L = eagle2_layout(c);
+  const E2Params p = make_params(c, L, state);
+  if (c->B == 0) return SV_OK;
+  hipLaunchKernelGGL(k_row_topk, dim3(c->B * c->k * L.nsplit), dim3(kTopkThreads), 0, s, p, q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) { set_error("eagle2 top-k launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  hipLaunchKernelGGL(k_expand, dim3(c->B), dim3(kE2Threads), 0, s, p, step, frontier, frontier_tokens);
+  e = hipGetLastError();
+  if (e != hipSuccess) { set_error("eagle2 expand launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  return SV_OK;
+}
+
+sv_status launch_eagle2_finish(const sv_eagle2_cfg* c, const void* state, int32_t* parent, int32_t* tokens,
+                               int32_t* num_nodes, int32_t* q_row, int32_t* status, hipStream_t s) {
+  const E2Layout L = eagle2_layout(c);
+  const E2Params p = make_params(c, L, const_cast<void*>(state));
+  if (c->B == 0) return SV_OK;
+  hipLaunchKernelGGL(k_finish, dim3(c->B), dim3(kFinishThreads), 0, s, p, parent, tokens, num_nodes, q_row, status);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) { set_error("eagle2 finish launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  return SV_OK;
+}
+
+}  // namespace sv

@@ -122,6 +122,29 @@ sv_status check_commit(const sv_tree* t, const sv_commit_args* c) {
   return SV_OK;
 }
 
+sv_status check_eagle2(const sv_eagle2_cfg* c) {
+  if (!c) { set_error("tree-builder config is NULL"); return SV_E_NULL; }
+  if (c->B < 0 || c->k < 1 || c->depth < 1 || c->V < 1 || c->m < 1) {
+    set_error("tree builder B=%d V=%d k=%d depth=%d m=%d", c->B, c->V, c->k, c->depth, c->m);
+    return SV_E_SHAPE;
+  }
+  if (c->k > 16 || c->V < c->k) { set_error("tree builder k=%d (need 1..16 and <= V=%d)", c->k, c->V); return SV_E_UNSUPPORTED; }
+  const long nmax = 1L + c->k + (long)(c->depth - 1) * c->k * c->k;
+  if (c->depth > 4096 || nmax > 2048) { set_error("tree builder: %ld nodes before the rerank (max 2048)", nmax); return SV_E_UNSUPPORTED; }
+  if (c->m > nmax - 1) { set_error("tree builder m=%d > %ld generated draft nodes", c->m, nmax - 1); return SV_E_SHAPE; }
+  if (c->m + 1 > kMaxT) { set_error("tree builder m+1=%d > %d verify positions", c->m + 1, kMaxT); return SV_E_UNSUPPORTED; }
+  if ((long)c->B * c->k * 16 > 0x7FFFFFFFL || (long)c->B * nmax > 0x7FFFFFFFL) { set_error("tree builder B too large"); return SV_E_UNSUPPORTED; }
+  return SV_OK;
+}
+
+sv_status check_state(const sv_eagle2_cfg* c, const void* state, size_t state_bytes) {
+  const size_t need = eagle2_layout(c).bytes;
+  if (!state) { set_error("tree-builder state is NULL"); return SV_E_NULL; }
+  if (state_bytes < need) { set_error("tree-builder state %zu bytes < %zu needed", state_bytes, need); return SV_E_WORKSPACE; }
+  if (!aligned(state, kWsAlign)) { set_error("tree-builder state not %zu-byte aligned", kWsAlign); return SV_E_WORKSPACE; }
+  return SV_OK;
+}
+
 sv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return SV_OK;
   if (!ws) { set_error("workspace is NULL (need %zu bytes)", need); return SV_E_WORKSPACE; }
@@ -206,6 +229,50 @@ sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const in
   return launch_commit(tree, tree_status, out_nodes, out_count, c, (hipStream_t)stream);
 }
 
+size_t sv_eagle2_state_bytes(const sv_eagle2_cfg* c) {
+  clear_error();
+  if (check_eagle2(c)) return 0;
+  return eagle2_layout(c).bytes;
+}
+
+sv_status sv_eagle2_begin(const sv_eagle2_cfg* c, void* state, size_t state_bytes, const int32_t* root_tokens,
+                          void* stream) {
+  clear_error();
+  sv_status st;
+  if ((st = check_eagle2(c))) return st;
+  if (c->B == 0) return SV_OK;
+  if ((st = check_state(c, state, state_bytes))) return st;
+  if (!root_tokens) { set_error("root_tokens is NULL"); return SV_E_NULL; }
+  return launch_eagle2_begin(c, state, root_tokens, (hipStream_t)stream);
+}
+
+sv_status sv_eagle2_expand(const sv_eagle2_cfg* c, void* state, size_t state_bytes, int32_t step, const float* q,
+                           int32_t* frontier, int32_t* frontier_tokens, void* stream) {
+  clear_error();
+  sv_status st;
+  if ((st = check_eagle2(c))) return st;
+  if (step < 0 || step >= c->depth) { set_error("step %d outside [0, %d)", step, c->depth); return SV_E_SHAPE; }
+  if (c->B == 0) return SV_OK;
+  if ((st = check_state(c, state, state_bytes))) return st;
+  if (!q) { set_error("q is NULL"); return SV_E_NULL; }
+  if (!aligned(q, 16)) { set_error("q must be 16-byte aligned"); return SV_E_UNSUPPORTED; }
+  return launch_eagle2_expand(c, state, step, q, frontier, frontier_tokens, (hipStream_t)stream);
+}
+
+sv_status sv_eagle2_finish(const sv_eagle2_cfg* c, const void* state, size_t state_bytes, int32_t* parent,
+                           int32_t* tokens, int32_t* num_nodes, int32_t* q_row, int32_t* status, void* stream) {
+  clear_error();
+  sv_status st;
+  if ((st = check_eagle2(c))) return st;
+  if (c->B == 0) return SV_OK;
+  if ((st = check_state(c, state, state_bytes))) return st;
+  if (!parent || !tokens || !num_nodes || !q_row || !status) {
+    set_error("parent/tokens/num_nodes/q_row/status is NULL");
+    return SV_E_NULL;
+  }
+  return launch_eagle2_finish(c, state, parent, tokens, num_nodes, q_row, status, (hipStream_t)stream);
+}
+
 size_t sv_workspace_bytes(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc) {
   clear_error();
   // sizing reads only the scalar fields: pointers may be NULL here
@@ -249,6 +316,7 @@ const char* sv_status_string(sv_status s) {
     case SV_TREE_E_SYNC: return "tree: cross-workgroup wait timed out";
     case SV_TREE_E_CACHE: return "commit: no room in the cache";
     case SV_TREE_E_PATH: return "commit: accepted path out of range";
+    case SV_TREE_E_PROB: return "tree builder: draft probability outside [0, 1] or NaN";
     default: return "unknown status";
   }
 }

@@ -60,6 +60,21 @@ sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_
 sv_status launch_commit(const sv_tree* t, int32_t* tree_status, const int32_t* out_nodes,
                         const int32_t* out_count, const sv_commit_args* a, hipStream_t s);
 
+// ---------------------------------------------------------------- tree builder
+struct E2Layout {
+  int nmax;         // nodes per sequence: 1 + k + (depth - 1) k^2
+  int nsplit;       // vocabulary chunks per probability row
+  int chunk;        // tokens per chunk (multiple of 4)
+  size_t off_seq, off_front, off_parent, off_token, off_depth, off_rank, off_qrow, off_value, off_cand, off_bad;
+  size_t bytes;
+};
+E2Layout eagle2_layout(const sv_eagle2_cfg* c);
+sv_status launch_eagle2_begin(const sv_eagle2_cfg* c, void* state, const int32_t* root_tokens, hipStream_t s);
+sv_status launch_eagle2_expand(const sv_eagle2_cfg* c, void* state, int step, const float* q, int32_t* frontier,
+                               int32_t* frontier_tokens, hipStream_t s);
+sv_status launch_eagle2_finish(const sv_eagle2_cfg* c, const void* state, int32_t* parent, int32_t* tokens,
+                               int32_t* num_nodes, int32_t* q_row, int32_t* status, hipStream_t s);
+
 // ---------------------------------------------------------------- mask
 sv_status launch_mask(const sv_tree* t, uint64_t* anc, int32_t* depth, int32_t* tree_status,
                       hipStream_t s);

@@ -7,8 +7,9 @@ the current torch stream.  Nothing here computes any part of the verification.
 """
 import numpy as np
 
-from . import (SV_SIB_IID, SV_SIB_WITHOUT_REPLACEMENT, make_accept_args, make_attn_args, make_commit_args,
-               make_tree, sv_commit_accepted, sv_spec_accept, sv_tree_attn, sv_tree_mask_build, sv_verify_step,
+from . import (SV_SIB_IID, SV_SIB_WITHOUT_REPLACEMENT, SvEagle2Cfg, make_accept_args, make_attn_args,
+               make_commit_args, make_tree, sv_commit_accepted, sv_eagle2_begin, sv_eagle2_expand, sv_eagle2_finish,
+               sv_eagle2_state_bytes, sv_spec_accept, sv_tree_attn, sv_tree_mask_build, sv_verify_step,
                sv_workspace_bytes)
 
 
@@ -123,3 +124,42 @@ class DeviceProblem:
         return dict(out_nodes=self.out_nodes.cpu().numpy(), out_tokens=self.out_tokens.cpu().numpy(),
                     out_count=self.out_count.cpu().numpy(), out_passes=self.out_passes.cpu().numpy(),
                     status=self.status.cpu().numpy())
+
+
+class DeviceTreeBuilder:
+    """State and outputs of the EAGLE-2 tree builder for one batch on one GPU.
+
+    ``run(q_steps, root_tokens)`` takes one device float32 tensor [B][k][V] per
+    expansion step (the drafter's probability rows for that step's frontier)
+    and calls begin, expand for every step and finish on the current stream.
+    """
+
+    def __init__(self, B, V, k, depth, m, device="cuda"):
+        import torch
+        self.cfg = SvEagle2Cfg(B, V, k, depth, m)
+        n = sv_eagle2_state_bytes(self.cfg)
+        if n == 0:
+            raise ValueError("unsupported tree-builder configuration")
+        self.state = torch.empty((n,), dtype=torch.uint8, device=device)
+        i32 = dict(dtype=torch.int32, device=device)
+        T = m + 1
+        self.frontier = torch.full((depth, B, k), -7, **i32)
+        self.frontier_tokens = torch.full((depth, B, k), -7, **i32)
+        self.parent = torch.full((B, T), -7, **i32)
+        self.tokens = torch.full((B, T), -7, **i32)
+        self.q_row = torch.full((B, T), -7, **i32)
+        self.num_nodes = torch.full((B,), -7, **i32)
+        self.status = torch.full((B,), -7, **i32)
+
+    def run(self, q_steps, root_tokens, stream=None):
+        sv_eagle2_begin(self.cfg, self.state, root_tokens, stream)
+        for s in range(self.cfg.depth):
+            sv_eagle2_expand(self.cfg, self.state, s, q_steps[s], self.frontier[s], self.frontier_tokens[s], stream)
+        sv_eagle2_finish(self.cfg, self.state, self.parent, self.tokens, self.num_nodes, self.q_row, self.status,
+                         stream)
+
+    def results(self):
+        return dict(parent=self.parent.cpu().numpy(), tokens=self.tokens.cpu().numpy(),
+                    q_row=self.q_row.cpu().numpy(), num_nodes=self.num_nodes.cpu().numpy(),
+                    status=self.status.cpu().numpy(), frontier=self.frontier.cpu().numpy(),
+                    frontier_tokens=self.frontier_tokens.cpu().numpy())

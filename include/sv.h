@@ -72,7 +72,8 @@ enum {
   SV_TREE_E_NOQ = 6,       /* temperature[b] > 0 but q_probs is NULL                  */
   SV_TREE_E_SYNC = 7,      /* internal: a cross-workgroup wait timed out              */
   SV_TREE_E_CACHE = 8,     /* commit: L_b + out_count[b] exceeds L_max (or L_b < 0)   */
-  SV_TREE_E_PATH = 9       /* commit: out_count[b] > T_b or a path entry outside [1, T_b) */
+  SV_TREE_E_PATH = 9,      /* commit: out_count[b] > T_b or a path entry outside [1, T_b) */
+  SV_TREE_E_PROB = 10      /* tree builder: a draft probability outside [0, 1] or NaN  */
 };
 
 /* Element types. */
@@ -225,6 +226,65 @@ typedef struct {
  * Needs no workspace.  Tensors must be 16-byte aligned. */
 sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const int32_t* out_nodes,
                              const int32_t* out_count, const sv_commit_args* c, void* stream);
+
+/* ---------------------------------------------------------------- tree builder
+ * EAGLE-2 draft-tree construction ([EAGLE article] sec. 2.3 "Context-aware
+ * draft tree"; sec. 2.2 for draft confidence as the acceptance estimate).
+ * A node's value is the product of the draft probabilities along its path
+ * from the root (value 1).  Each step expands the k best nodes of the newest
+ * layer ("Expansion Phase"): the drafter's probability row of each such node
+ * gives it k children, its k most probable tokens (probability descending,
+ * ties to the lower token id).  After the last step the m best draft nodes
+ * over the whole tree are kept ("Reranking Phase": value descending, equal
+ * values to the shallower node, then to the earlier created), which is a
+ * connected tree because a child's value never exceeds its parent's, and the
+ * kept tree is flattened for verification: by depth, then parent position,
+ * then sibling rank, so parents precede children (the parent array that
+ * sv_tree_mask_build takes).  Values are float32 products, one IEEE multiply
+ * per node; every selection compares them exactly.
+ *
+ * Use: sv_eagle2_begin, then for step = 0 .. depth-1 run the drafter on the
+ * current frontier (the root at step 0) and call sv_eagle2_expand with its
+ * probability rows, then sv_eagle2_finish.  All calls only enqueue work on the
+ * stream; the state lives in one caller buffer of sv_eagle2_state_bytes bytes
+ * (256-byte aligned), and calls on one state must be in this order. */
+typedef struct {
+  int32_t B;       /* sequences                                                      */
+  int32_t V;       /* vocabulary size (>= k)                                          */
+  int32_t k;       /* expansion width: nodes expanded per step and children per node, 1..16 */
+  int32_t depth;   /* expansion steps, >= 1                                           */
+  int32_t m;       /* draft nodes kept, 1 <= m <= k + (depth-1) k^2 and m + 1 <= 256;
+                      the tree has k + (depth-1) k^2 + 1 <= 2048 nodes before the rerank */
+} sv_eagle2_cfg;
+
+/* State bytes for a configuration (host only); 0 if it is invalid or
+ * unsupported (see sv_last_error). */
+size_t sv_eagle2_state_bytes(const sv_eagle2_cfg* c);
+
+/* Starts the trees: node 0 of sequence b is root_tokens[b] (device [B] int32)
+ * with value 1; the frontier is the root. */
+sv_status sv_eagle2_begin(const sv_eagle2_cfg* c, void* state, size_t state_bytes,
+                          const int32_t* root_tokens, void* stream);
+
+/* One expansion step.  q (device, float32 [B][k][V], 16-byte aligned): row j
+ * of sequence b is the drafter's probability row for frontier entry j (only
+ * row 0, the root's, at step 0; rows beyond the frontier are not read).
+ * Every row that is read is checked: a value outside [0, 1] or NaN sets the
+ * sequence's status to SV_TREE_E_PROB and its later steps do nothing.
+ * frontier (device int32 [B][k], may be NULL): the node ids of the next
+ * frontier, -1 padded; frontier_tokens (device int32 [B][k], may be NULL):
+ * their tokens, -1 padded.  step must count 0, 1, ..., depth-1. */
+sv_status sv_eagle2_expand(const sv_eagle2_cfg* c, void* state, size_t state_bytes, int32_t step,
+                           const float* q, int32_t* frontier, int32_t* frontier_tokens, void* stream);
+
+/* The rerank and flattening.  Outputs (device, int32): parent, tokens, q_row
+ * [B][m+1] and num_nodes, status [B].  Position 0 is the root (parent -1).
+ * q_row[b][i] = step * k + j when the node at position i was frontier entry j
+ * of that step (its draft probabilities are row j of that step's q), else -1.
+ * A sequence with status SV_TREE_E_PROB gets num_nodes 0 and -1 elsewhere. */
+sv_status sv_eagle2_finish(const sv_eagle2_cfg* c, const void* state, size_t state_bytes,
+                           int32_t* parent, int32_t* tokens, int32_t* num_nodes, int32_t* q_row,
+                           int32_t* status, void* stream);
 
 /* Workspace bytes needed by sv_tree_attn (attn != NULL), sv_spec_accept
  * (acc != NULL) or both (the maximum).  Host only; reads only the scalar

@@ -264,3 +264,26 @@ def make_instance(spec, seed=0, with_attn=True, with_accept=True):
     inst.u_accept = r_unif.random(size=(B, T_max), dtype=np.float32)
     inst.u_sample = r_unif.random(size=(B, T_max), dtype=np.float32)
     return inst
+
+
+def make_draft_rows(B, k, depth, V, seed=0, draft_std=3.0, tie_step=None, cfg_id=900):
+    """Synthetic drafter output for the tree builder: for each expansion step
+    s, a float32 array [B][k][V] whose row j is the probability row the drafter
+    gives for frontier entry j, ``softmax(N(0, draft_std^2))`` computed in
+    float64.  The rows do not depend on which node they end up attached to
+    (that is decided by the builder).  With ``tie_step`` set, probabilities are
+    rounded down to multiples of ``tie_step`` so that equal values (ties) are
+    common.  Seeded by ``SeedSequence([cfg_id, seed])``, one Philox stream per
+    step."""
+    streams = np.random.SeedSequence([cfg_id, int(seed)]).spawn(depth)
+    out = []
+    for s in range(depth):
+        rng = np.random.Generator(np.random.Philox(streams[s]))
+        z = rng.standard_normal((B, k, V)) * draft_std
+        z -= z.max(axis=2, keepdims=True)
+        p = np.exp(z)
+        p /= p.sum(axis=2, keepdims=True)
+        if tie_step is not None:
+            p = np.floor(p / tie_step) * tie_step
+        out.append(p.astype(np.float32))
+    return out

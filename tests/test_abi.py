@@ -41,7 +41,7 @@ def test_binding_constants_match_header():
 
 
 def test_status_strings():
-    for code in list(range(-6, 1)) + list(range(1, 8)):
+    for code in list(range(-6, 1)) + list(range(1, 11)):
         s = sv.sv_status_string(code)
         assert s and s != "unknown status"
     assert sv.sv_status_string(99) == "unknown status"
@@ -114,3 +114,49 @@ def test_workspace_sizes_for_the_workloads():
         n_both = sv.sv_workspace_bytes(t, a, acc)
         assert n_acc > 0 and n_both >= n_acc
         assert n_both % 256 == 0
+
+
+# ---------------------------------------------------------------- tree builder (host checks only)
+def _e2(**kw):
+    c = sv.SvEagle2Cfg(4, 1000, 8, 6, 64)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_eagle2_state_bytes_and_config_checks():
+    n = sv.sv_eagle2_state_bytes(_e2())
+    assert n > 0 and n % 256 == 0
+    # nodes before the rerank: 1 + k + (depth-1) k^2
+    assert sv.sv_eagle2_state_bytes(_e2(m=255)) > 0                 # 256 verify positions
+    assert sv.sv_eagle2_state_bytes(_e2(k=2, depth=2, m=6)) > 0      # all 2 + 4 generated nodes
+    for bad in (dict(k=0), dict(k=17), dict(V=4, k=8), dict(m=0), dict(k=2, depth=2, m=7), dict(depth=0),
+                dict(m=256),
+                dict(k=16, depth=9, m=100), dict(k=16, depth=3, m=256), dict(B=-1)):
+        assert sv.sv_eagle2_state_bytes(_e2(**bad)) == 0, bad
+        assert sv.sv_last_error()
+
+
+def test_eagle2_entry_points_reject_bad_host_arguments():
+    c = _e2()
+    need = sv.sv_eagle2_state_bytes(c)
+    L = sv.lib()
+    fake = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100004)
+    # state: NULL, too small, misaligned
+    assert L.sv_eagle2_begin(ctypes.byref(c), None, need, fake, None) == sv.SV_E_NULL
+    assert L.sv_eagle2_begin(ctypes.byref(c), fake, need - 1, fake, None) == sv.SV_E_WORKSPACE
+    assert L.sv_eagle2_begin(ctypes.byref(c), ctypes.c_void_p(0x100010), need, fake, None) == sv.SV_E_WORKSPACE
+    assert L.sv_eagle2_begin(ctypes.byref(c), fake, need, None, None) == sv.SV_E_NULL
+    # expand: step range, q NULL / misaligned
+    assert L.sv_eagle2_expand(ctypes.byref(c), fake, need, -1, fake, None, None, None) == sv.SV_E_SHAPE
+    assert L.sv_eagle2_expand(ctypes.byref(c), fake, need, 6, fake, None, None, None) == sv.SV_E_SHAPE
+    assert L.sv_eagle2_expand(ctypes.byref(c), fake, need, 0, None, None, None, None) == sv.SV_E_NULL
+    assert L.sv_eagle2_expand(ctypes.byref(c), fake, need, 0, odd, None, None, None) == sv.SV_E_UNSUPPORTED
+    # finish: every output is required
+    assert L.sv_eagle2_finish(ctypes.byref(c), fake, need, fake, fake, fake, fake, None, None) == sv.SV_E_NULL
+    bad = _e2(k=0)
+    assert L.sv_eagle2_finish(ctypes.byref(bad), fake, need, fake, fake, fake, fake, fake, None) == sv.SV_E_SHAPE
+    # B = 0: nothing to do, no pointer is looked at
+    z = _e2(B=0)
+    assert L.sv_eagle2_begin(ctypes.byref(z), None, 0, None, None) == sv.SV_OK
