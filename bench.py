@@ -179,6 +179,35 @@ def time_commit(dev, inst, res, n, stream):
     return ms, float(2 * 2 * rows * inst.Hkv * inst.D * s)     # K and V rows, read and written
 
 
+def time_eagle2(inst, n, stream):
+    """One EAGLE-2 tree build (begin, one expand per step, finish) for the
+    batch: k = 8, 6 steps, m = T_max - 1 kept nodes (the batch's tree size),
+    synthetic probability rows made on the device.  Returns a dict with the
+    build time, the probability bytes it reads and their rate."""
+    import torch
+    from eagle_tree_verification_attn_amd.problem import DeviceTreeBuilder
+    B, V, k, depth, m = inst.B, inst.V, 8, 6, inst.T_max - 1
+    g = torch.Generator(device="cuda").manual_seed(7)
+    q = []
+    for _ in range(depth):
+        z = torch.randn((B, k, V), generator=g, device="cuda", dtype=torch.float32) * 3.0
+        q.append(torch.softmax(z, dim=2).contiguous())
+        del z
+    roots = torch.arange(B, dtype=torch.int32, device="cuda")
+    tb = DeviceTreeBuilder(B, V, k, depth, m)
+    for _ in range(3):
+        tb.run(q, roots, stream)
+    ms = time_launches(lambda: tb.run(q, roots, stream), n, stream)
+    ok = int((tb.status == 0).sum().item())
+    rows = B * (1 + (depth - 1) * k)          # the root's row, then k rows per later step
+    nbytes = float(rows * V * 4)
+    del q
+    return {"workload": f"eagle2_build_b{B}_k{k}_d{depth}_m{m}", "ms": round(ms, 5), "q_bytes": nbytes,
+            "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "sequences_ok": ok, "note": "before the step, not part of it"}
+
+
 def cpu_baseline(inst, seconds):
     """The oracle on a bounded sample: whole sequences (attention for all heads,
     target softmax and walk), scaled to steps/s of the full batch."""
@@ -285,6 +314,7 @@ def main():
     # the commit of the accepted path (not part of the step): into caches with
     # room after the prefix, so the step's own caches stay as they are
     commit_ms, commit_bytes = time_commit(dev, inst, res, n, stream)
+    e2 = time_eagle2(inst, n, stream)
     flops, attn_bytes = algorithmic_work(inst)
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
@@ -324,6 +354,7 @@ def main():
                        "spec_accept": round(acc_ms, 5)},
         "commit_accepted": {"ms": round(commit_ms, 5), "bytes": commit_bytes,
                             "note": "after the step, not part of it"},
+        "eagle2_build": e2,
         "hbm_roofline": {"tree_attn_verify": {"algorithmic_bytes": attn_bytes,
                                               "GB_s": round(attn_gbs, 1),
                                               "frac": round(attn_gbs / HBM_PEAK_GBS, 4)},

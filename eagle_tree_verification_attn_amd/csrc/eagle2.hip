@@ -5,11 +5,16 @@
 // verification).
 //
 // Three kernels:
-//   k_row_topk     one workgroup per (sequence, frontier row, vocabulary
-//                  chunk): streams the chunk of the drafter's probability row
-//                  once, keeps each thread's k best (probability, token) keys
-//                  in registers, merges them across the block and checks the
-//                  range.  This is the HBM-bound part.
+//   k_row_topk     one workgroup per (sequence, frontier row, 8192-token
+//                  chunk): reads the chunk of the drafter's probability row
+//                  once into registers and checks the range.  In each wave
+//                  the k-th largest of the lanes' maxima bounds the chunk's
+//                  k-th largest key from below (those k maxima are k keys at
+//                  least that large); the largest of the waves' bounds is
+//                  used, only keys at or above it are gathered in LDS and
+//                  ranked exactly (when very many keys tie at that bound, k
+//                  rounds of a block maximum instead).  This is the HBM-bound
+//                  part.
 //   k_expand       one workgroup per sequence: merges the chunks' keys of each
 //                  frontier row, appends the children (value = parent value x
 //                  probability, one float32 multiply) and ranks the new layer
@@ -26,7 +31,12 @@
 namespace sv {
 
 constexpr int kTopkThreads = 256;
+constexpr int kE2Chunk = 8192;                       // tokens per top-k workgroup
+constexpr int kEPT = kE2Chunk / kTopkThreads;        // elements per thread (32)
+constexpr int kCandCap = 1024;                       // gathered candidates per chunk
 constexpr int kE2MaxK = 16;
+constexpr int kE2MaxSplit = 64;                      // chunks per row: V <= 64 * 8192
+constexpr int kE2StageKeys = kE2MaxSplit * kE2MaxK;  // 1024 keys staged in LDS at a time
 constexpr int kE2Threads = 256;
 constexpr int kFinishThreads = 1024;
 
@@ -49,11 +59,9 @@ enum { kSeqN = 0, kSeqLayer = 1, kSeqFront = 2, kSeqStatus = 3 };
 E2Layout eagle2_layout(const sv_eagle2_cfg* c) {
   E2Layout L{};
   L.nmax = 1 + c->k + (c->depth - 1) * c->k * c->k;
-  L.nsplit = (c->V + 8191) / 8192;
-  if (L.nsplit > 16) L.nsplit = 16;
+  L.nsplit = (c->V + kE2Chunk - 1) / kE2Chunk;
   if (L.nsplit < 1) L.nsplit = 1;
-  L.chunk = (c->V + L.nsplit - 1) / L.nsplit;
-  L.chunk = (L.chunk + 3) / 4 * 4;
+  L.chunk = kE2Chunk;
   size_t o = 0;
   const size_t B = (size_t)c->B, N = (size_t)L.nmax, k = (size_t)c->k;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, kWsAlign); return at; };
@@ -96,25 +104,6 @@ __device__ inline uint64_t prob_key(float v, int tok) {
 __device__ inline float key_prob(uint64_t key) { return __uint_as_float((uint32_t)(key >> 32)); }
 __device__ inline int key_token(uint64_t key) { return (int)(~(uint32_t)key); }
 
-// Inserts key x into the descending list t[0..kE2MaxK) (entries past k are
-// don't-care); the caller has checked that x beats t[k - 1].
-__device__ inline void list_insert(uint64_t (&t)[kE2MaxK], uint64_t x) {
-#pragma unroll
-  for (int p = kE2MaxK - 1; p > 0; --p) {
-    const bool shift = x > t[p - 1];
-    const bool here = !shift && x > t[p];
-    t[p] = shift ? t[p - 1] : (here ? x : t[p]);
-  }
-  if (x > t[0]) t[0] = x;
-}
-
-__device__ inline uint64_t list_at(const uint64_t (&t)[kE2MaxK], int i) {
-  uint64_t r = 0;
-#pragma unroll
-  for (int p = 0; p < kE2MaxK; ++p) r = (p == i) ? t[p] : r;
-  return r;
-}
-
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -154,73 +143,115 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
   const int tid = threadIdx.x;
   const int32_t* s = p.seq + (size_t)b * 8;
   if (s[kSeqStatus] != SV_TREE_OK || j >= s[kSeqFront]) return;
-  const int lo = c * p.chunk;
-  const int hi = min(p.V, lo + p.chunk);
+  const int lo = c * kE2Chunk;
+  const int hi = min(p.V, lo + kE2Chunk);
   const float* row = q + ((size_t)b * p.k + j) * p.V;
-  uint64_t t[kE2MaxK];
+  const bool vec = (p.V & 3) == 0;
+  // element i of this thread: 16-byte runs when rows are 16-byte aligned
+  auto index = [&](int i) { return vec ? lo + 4 * (tid + kTopkThreads * (i >> 2)) + (i & 3) : lo + tid + kTopkThreads * i; };
+  float v[kEPT];
+  if (vec) {
 #pragma unroll
-  for (int i = 0; i < kE2MaxK; ++i) t[i] = 0;
-  uint64_t thr = 0;       // t[k - 1]
-  bool bad = false;
-  auto consider = [&](float v, int i) {
-    bad |= !(v >= 0.0f && v <= 1.0f);
-    const uint64_t key = prob_key(v, i);
-    if (key > thr) {
-      list_insert(t, key);
-      thr = list_at(t, p.k - 1);
-    }
-  };
-  if ((p.V & 3) == 0 && (lo & 3) == 0) {
-    const float4* r4 = reinterpret_cast<const float4*>(row + lo);
-    const int n4 = (hi - lo) >> 2;
-    int i = tid;
-    for (; i + 3 * kTopkThreads < n4; i += 4 * kTopkThreads) {
-      float4 v[4];
+    for (int i4 = 0; i4 < kEPT / 4; ++i4) {
+      const int e = lo + 4 * (tid + kTopkThreads * i4);
+      if (e + 3 < hi) {
+        const float4 x = *reinterpret_cast<const float4*>(row + e);
+        v[4 * i4] = x.x; v[4 * i4 + 1] = x.y; v[4 * i4 + 2] = x.z; v[4 * i4 + 3] = x.w;
+      } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = r4[i + u * kTopkThreads];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lo + 4 * (i + u * kTopkThreads);
-        consider(v[u].x, e);
-        consider(v[u].y, e + 1);
-        consider(v[u].z, e + 2);
-        consider(v[u].w, e + 3);
+        for (int u = 0; u < 4; ++u) v[4 * i4 + u] = e + u < hi ? row[e + u] : 0.0f;
       }
     }
-    for (; i < n4; i += kTopkThreads) {
-      const float4 v = r4[i];
-      const int e = lo + 4 * i;
-      consider(v.x, e);
-      consider(v.y, e + 1);
-      consider(v.z, e + 2);
-      consider(v.w, e + 3);
-    }
-    for (int e = lo + 4 * n4 + tid; e < hi; e += kTopkThreads) consider(row[e], e);
   } else {
-    for (int e = lo + tid; e < hi; e += kTopkThreads) consider(row[e], e);
+#pragma unroll
+    for (int i = 0; i < kEPT; ++i) {
+      const int e = lo + tid + kTopkThreads * i;
+      v[i] = e < hi ? row[e] : 0.0f;
+    }
   }
-  // block merge: k rounds, each taking the best head among the threads
+  bool bad = false;
+  uint64_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < kEPT; ++i) {
+    const int e = index(i);
+    if (e < hi) {
+      bad |= !(v[i] >= 0.0f && v[i] <= 1.0f);
+      const uint64_t key = prob_key(v[i], e);
+      mx = key > mx ? key : mx;
+    }
+  }
+  __shared__ uint64_t keys_s[kTopkThreads];
+  __shared__ uint64_t cand_s[kCandCap];
   __shared__ uint64_t wmax[kTopkThreads / 64];
-  __shared__ int bad_s;
-  if (tid == 0) bad_s = 0;
+  __shared__ uint64_t t0_s[kTopkThreads / 64];
+  __shared__ int ncand_s, bad_s;
+  uint64_t* out = p.cand + (((size_t)b * p.k + j) * p.nsplit + c) * p.k;
+  if (tid == 0) { ncand_s = 0; bad_s = 0; }
+  if (tid < kTopkThreads / 64) t0_s[tid] = 0;
+  if (tid < p.k) out[tid] = 0;
+  keys_s[tid] = mx;
   __syncthreads();
   if (bad) bad_s = 1;
-  uint64_t* out = p.cand + (((size_t)b * p.k + j) * p.nsplit + c) * p.k;
-  for (int r = 0; r < p.k; ++r) {
-    const uint64_t w = wave_max_u64(t[0]);
-    if ((tid & 63) == 0) wmax[tid >> 6] = w;
-    __syncthreads();
-    uint64_t best = 0;
+  // per wave, the k-th largest of its lanes' maxima (0 when fewer than k lanes
+  // hold a token): nonzero maxima are distinct keys, so one lane has rank k - 1
+  {
+    const uint64_t* ws = keys_s + (tid & ~63);
+    int r = 0;
+#pragma unroll 8
+    for (int e = 0; e < 64; ++e) r += ws[e] > mx;
+    if (mx != 0 && r == p.k - 1) t0_s[tid >> 6] = mx;
+  }
+  __syncthreads();
+  uint64_t t0 = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkThreads / 64; ++i) best = wmax[i] > best ? wmax[i] : best;
-    __syncthreads();
-    if (tid == 0) out[r] = best;
-    if (best != 0 && t[0] == best) {   // keys are distinct (tokens differ): one owner pops
+  for (int w = 0; w < kTopkThreads / 64; ++w) t0 = t0_s[w] > t0 ? t0_s[w] : t0;
+  int mine = 0;
 #pragma unroll
-      for (int i = 0; i < kE2MaxK - 1; ++i) t[i] = t[i + 1];
-      t[kE2MaxK - 1] = 0;
+  for (int i = 0; i < kEPT; ++i) mine += index(i) < hi && prob_key(v[i], index(i)) >= t0;
+  int at = mine ? atomicAdd(&ncand_s, mine) : 0;
+#pragma unroll
+  for (int i = 0; i < kEPT; ++i) {
+    const int e = index(i);
+    const uint64_t key = prob_key(v[i], e);
+    if (e < hi && key >= t0) {
+      if (at < kCandCap) cand_s[at] = key;
+      ++at;
     }
   }
+  __syncthreads();
+  const int C = ncand_s;
+  if (C <= kCandCap) {
+    for (int x = tid; x < C; x += kTopkThreads) {
+      const uint64_t key = cand_s[x];
+      int r = 0;
+#pragma unroll 8
+      for (int e = 0; e < C; ++e) r += cand_s[e] > key;
+      if (r < p.k) out[r] = key;
+    }
+  } else {
+    // very many keys tie at the bound: k rounds, each the block's largest key
+    // below the previous round's
+    uint64_t prev = ~0ull;
+    for (int r = 0; r < p.k; ++r) {
+      uint64_t m = 0;
+#pragma unroll
+      for (int i = 0; i < kEPT; ++i) {
+        const int e = index(i);
+        const uint64_t key = prob_key(v[i], e);
+        if (e < hi && key < prev && key > m) m = key;
+      }
+      const uint64_t w = wave_max_u64(m);
+      if ((tid & 63) == 0) wmax[tid >> 6] = w;
+      __syncthreads();
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < kTopkThreads / 64; ++i) best = wmax[i] > best ? wmax[i] : best;
+      __syncthreads();
+      if (tid == 0) out[r] = best;
+      prev = best;
+    }
+  }
+  __syncthreads();
   if (tid == 0) p.cand_bad[((size_t)b * p.k + j) * p.nsplit + c] = bad_s;
 }
 
@@ -233,6 +264,9 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
   const size_t nb = (size_t)b * p.nmax;
   const int k = p.k;
   __shared__ uint64_t best_s[kE2MaxK][kE2MaxK];   // per frontier row, its k best keys
+  __shared__ uint64_t row_s[kE2StageKeys];            // chunk candidates of a group of rows
+  __shared__ float fval_s[kE2MaxK];
+  __shared__ int fnode_s[kE2MaxK], fdep_s[kE2MaxK];
   __shared__ float val_s[kE2MaxK * kE2MaxK];     // the new layer's values
   __shared__ int bad_s;
   const int status = s[kSeqStatus];
@@ -256,33 +290,48 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
     if (tid == 0) s[kSeqStatus] = SV_TREE_E_COUNT;
   }
   if (ok) {
-    // merge: candidate e of row j ranks by the number of row-j candidates above it
+    // merge: candidate e of row j ranks by the number of row-j candidates
+    // above it; rows are staged in LDS a group at a time
     const int C = p.nsplit * k;
-    for (int i = tid; i < F * C; i += kE2Threads) {
-      const int j = i / C;
-      const uint64_t* cj = p.cand + (size_t)(b * k + j) * C;
-      const uint64_t x = cj[i % C];
-      int r = 0;
-      for (int e = 0; e < C; ++e) r += cj[e] > x;
-      if (x != 0 && r < k) best_s[j][r] = x;
+    const int rows = kE2StageKeys / C;                 // >= 1 (C <= 1024)
+    if (tid < F) {
+      const int node = p.front[(size_t)b * 16 + tid];
+      fnode_s[tid] = node;
+      fval_s[tid] = p.value[nb + node];
+      fdep_s[tid] = p.depthv[nb + node];
     }
-    __syncthreads();
+    for (int j0 = 0; j0 < F; j0 += rows) {
+      const int nr = min(rows, F - j0);
+      const uint64_t* cj = p.cand + (size_t)(b * k + j0) * C;
+      for (int i = tid; i < nr * C; i += kE2Threads) row_s[i] = cj[i];
+      __syncthreads();
+      for (int i = tid; i < nr * C; i += kE2Threads) {
+        const int jj = i / C;
+        const uint64_t* rs = row_s + jj * C;
+        const uint64_t x = row_s[i];
+        int r = 0;
+#pragma unroll 8
+        for (int e = 0; e < C; ++e) r += rs[e] > x;
+        if (x != 0 && r < k) best_s[j0 + jj][r] = x;
+      }
+      __syncthreads();
+    }
     // children of frontier entry j: ids n0 + j k + r
     for (int i = tid; i < F * k; i += kE2Threads) {
       const int j = i / k, r = i % k;
-      const int par = p.front[(size_t)b * 16 + j];
+      const int par = fnode_s[j];
       const uint64_t key = best_s[j][r];
-      const float v = __fmul_rn(p.value[nb + par], key_prob(key));
+      const float v = __fmul_rn(fval_s[j], key_prob(key));
       const size_t id = nb + n0 + i;
       p.parent[id] = par;
       p.token[id] = key_token(key);
-      p.depthv[id] = p.depthv[nb + par] + 1;
+      p.depthv[id] = fdep_s[j] + 1;
       p.rank[id] = r;
       p.qrow[id] = -1;
       p.value[id] = v;
       val_s[i] = v;
     }
-    for (int j = tid; j < F; j += kE2Threads) p.qrow[nb + p.front[(size_t)b * 16 + j]] = step * k + j;
+    for (int j = tid; j < F; j += kE2Threads) p.qrow[nb + fnode_s[j]] = step * k + j;
     __syncthreads();
     // next frontier: the k best of the new layer (value descending, then id)
     const int Lc = F * k;
@@ -291,6 +340,7 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
     for (int i = tid; i < Lc; i += kE2Threads) {
       const float v = val_s[i];
       int r = 0;
+#pragma unroll 8
       for (int e = 0; e < Lc; ++e) r += (val_s[e] > v) || (val_s[e] == v && e < i);
       if (r < k) p.front[(size_t)b * 16 + r] = n0 + i;
     }
@@ -317,8 +367,11 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
   __shared__ float val_s[kMaxNodes];
   __shared__ int dep_s[kMaxNodes];
   __shared__ int pos_s[kMaxNodes];      // flattened position, -1 if not kept
-  __shared__ int key_s[kMaxNodes];      // per depth pass: parent position * 16 + rank
-  __shared__ int cnt_s;
+  __shared__ int par_s[kMaxNodes];
+  __shared__ int rank_s[kMaxNodes];
+  __shared__ int kept_s[kMaxT];         // the kept draft nodes, in no particular order
+  __shared__ int kkey_s[kMaxT];         // per depth pass: parent position * 16 + rank, or -1
+  __shared__ int cnt_s, nkept_s;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t* s = p.seq + (size_t)b * 8;
@@ -329,6 +382,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
   if (status == SV_TREE_OK && (N - 1 < p.m || N > p.nmax)) status = SV_TREE_E_COUNT;   // too few steps ran
   if (tid == 0) status_out[b] = status;
   const bool ok = status == SV_TREE_OK;
+  if (tid == 0) nkept_s = 0;
   if (!ok) {
     for (int i = tid; i < T; i += kFinishThreads) {
       parent_out[(size_t)b * T + i] = -1;
@@ -341,6 +395,8 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
   for (int i = tid; i < N; i += kFinishThreads) {
     val_s[i] = p.value[nb + i];
     dep_s[i] = p.depthv[nb + i];
+    par_s[i] = p.parent[nb + i];
+    rank_s[i] = p.rank[nb + i];
     pos_s[i] = -1;
   }
   __syncthreads();
@@ -349,28 +405,34 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
     const float v = val_s[i];
     const int d = dep_s[i];
     int r = 0;
+#pragma unroll 8
     for (int e = 1; e < N; ++e) {
       const float ve = val_s[e];
       r += (ve > v) || (ve == v && (dep_s[e] < d || (dep_s[e] == d && e < i)));
     }
     pos_s[i] = r < p.m ? 0 : -1;      // 0 marks kept; the position comes below
+    if (r < p.m) kept_s[atomicAdd(&nkept_s, 1)] = i;
   }
   if (tid == 0) pos_s[0] = 0;
   __syncthreads();
   // positions depth by depth: after the earlier depths, ordered by parent
   // position then sibling rank
+  const int M = nkept_s;              // = m
   int base = 1;
   for (int d = 1; d <= p.depth; ++d) {
-    for (int i = 1 + tid; i < N; i += kFinishThreads)
-      key_s[i] = (dep_s[i] == d && pos_s[i] >= 0) ? pos_s[p.parent[nb + i]] * 16 + p.rank[nb + i] : -1;
+    for (int x = tid; x < M; x += kFinishThreads) {
+      const int i = kept_s[x];
+      kkey_s[x] = dep_s[i] == d ? pos_s[par_s[i]] * 16 + rank_s[i] : -1;
+    }
     if (tid == 0) cnt_s = 0;
     __syncthreads();
-    for (int i = 1 + tid; i < N; i += kFinishThreads) {
-      const int key = key_s[i];
+    for (int x = tid; x < M; x += kFinishThreads) {
+      const int key = kkey_s[x];
       if (key < 0) continue;
       int r = 0;
-      for (int e = 1; e < N; ++e) r += key_s[e] >= 0 && key_s[e] < key;
-      pos_s[i] = base + r;
+#pragma unroll 8
+      for (int e = 0; e < M; ++e) r += kkey_s[e] >= 0 && kkey_s[e] < key;
+      pos_s[kept_s[x]] = base + r;
       atomicAdd(&cnt_s, 1);
     }
     __syncthreads();
@@ -380,7 +442,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
   for (int i = tid; i < N; i += kFinishThreads) {
     const int ps = pos_s[i];
     if (ps < 0 || ps >= T) continue;
-    parent_out[(size_t)b * T + ps] = i == 0 ? -1 : pos_s[p.parent[nb + i]];
+    parent_out[(size_t)b * T + ps] = i == 0 ? -1 : pos_s[par_s[i]];
     tokens_out[(size_t)b * T + ps] = p.token[nb + i];
     q_row_out[(size_t)b * T + ps] = p.qrow[nb + i];
   }

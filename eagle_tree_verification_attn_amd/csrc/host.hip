@@ -129,6 +129,7 @@ sv_status check_eagle2(const sv_eagle2_cfg* c) {
     return SV_E_SHAPE;
   }
   if (c->k > 16 || c->V < c->k) { set_error("tree builder k=%d (need 1..16 and <= V=%d)", c->k, c->V); return SV_E_UNSUPPORTED; }
+  if (c->V > 64 * 8192) { set_error("tree builder V=%d > %d", c->V, 64 * 8192); return SV_E_UNSUPPORTED; }
   const long nmax = 1L + c->k + (long)(c->depth - 1) * c->k * c->k;
   if (c->depth > 4096 || nmax > 2048) { set_error("tree builder: %ld nodes before the rerank (max 2048)", nmax); return SV_E_UNSUPPORTED; }
   if (c->m > nmax - 1) { set_error("tree builder m=%d > %ld generated draft nodes", c->m, nmax - 1); return SV_E_SHAPE; }

@@ -250,7 +250,7 @@ sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const in
  * (256-byte aligned), and calls on one state must be in this order. */
 typedef struct {
   int32_t B;       /* sequences                                                      */
-  int32_t V;       /* vocabulary size (>= k)                                          */
+  int32_t V;       /* vocabulary size (k <= V <= 524288)                                */
   int32_t k;       /* expansion width: nodes expanded per step and children per node, 1..16 */
   int32_t depth;   /* expansion steps, >= 1                                           */
   int32_t m;       /* draft nodes kept, 1 <= m <= k + (depth-1) k^2 and m + 1 <= 256;

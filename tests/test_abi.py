@@ -131,7 +131,7 @@ def test_eagle2_state_bytes_and_config_checks():
     assert sv.sv_eagle2_state_bytes(_e2(m=255)) > 0                 # 256 verify positions
     assert sv.sv_eagle2_state_bytes(_e2(k=2, depth=2, m=6)) > 0      # all 2 + 4 generated nodes
     for bad in (dict(k=0), dict(k=17), dict(V=4, k=8), dict(m=0), dict(k=2, depth=2, m=7), dict(depth=0),
-                dict(m=256),
+                dict(m=256), dict(V=64 * 8192 + 1),
                 dict(k=16, depth=9, m=100), dict(k=16, depth=3, m=256), dict(B=-1)):
         assert sv.sv_eagle2_state_bytes(_e2(**bad)) == 0, bad
         assert sv.sv_last_error()
