@@ -194,6 +194,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     rvalid[qt] = rrow[qt] < valid_rows;
   }
 
+  const bool wave_active = row0 + wave * NT * 16 < valid_rows;
   if (row0 >= valid_rows || kbeg >= kend) {
     // Nothing to attend for this workgroup: write zeros (single range) or an
     // empty partial (m = -inf, l = 0, O = 0).
@@ -473,9 +474,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (it + kStages - 2 < nblk) wait_copies_and_sync<(kStages - 2) * CPB>();
     else wait_copies_and_sync<0>();
     if (it + kStages - 1 < nblk) issue_block(kbeg + (it + kStages - 1) * BK, (it + kStages - 1) % kStages);
-    scores(it);
-    softmax();
-    pv_product(it);
+    // a wave whose rows are all padding (the last row block of a unit) only
+    // copies and keeps the barriers, leaving its SIMD to the other waves
+    if (wave_active) {
+      scores(it);
+      softmax();
+      pv_product(it);
+    }
   }
 
   // ---- epilogue
