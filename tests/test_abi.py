@@ -160,3 +160,17 @@ def test_eagle2_entry_points_reject_bad_host_arguments():
     # B = 0: nothing to do, no pointer is looked at
     z = _e2(B=0)
     assert L.sv_eagle2_begin(ctypes.byref(z), None, 0, None, None) == sv.SV_OK
+
+
+def test_plain_c_client_builds_and_passes(tmp_path):
+    """The header and library serve a C program directly: gcc compiles a
+    client against include/sv.h, links libsv.so, and runs its host checks."""
+    src = os.path.join(ROOT, "tests", "abi_host_check.c")
+    exe = str(tmp_path / "abi_host_check")
+    libdir = os.path.dirname(sv.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), src,
+                        "-L", libdir, "-lsv", "-Wl,-rpath," + libdir, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "passed" in r.stdout
