@@ -678,10 +678,13 @@ struct Variant {
   float row_cost;  // relative cost of one padded row
 };
 // Instantiated MFMA shapes (head dim, 16-row tiles per wave, waves per group);
-// all of them fit two waves per SIMD.
+// all of them fit two waves per SIMD.  The row costs are measured times per
+// padded row relative to the best shape of the head dim (fewer tiles per wave
+// read the same K/V tiles from LDS for fewer MFMAs; one-wave groups share no
+// copies).
 const Variant kVariants[] = {
-    {128, 3, 4, 1.0f}, {128, 2, 4, 1.0f}, {128, 2, 1, 1.0f}, {128, 1, 1, 1.0f},
-    {64, 4, 4, 1.0f},  {64, 3, 4, 1.0f},  {64, 2, 1, 1.0f},  {64, 1, 1, 1.0f},
+    {128, 3, 4, 1.0f}, {128, 2, 4, 1.2f}, {128, 2, 1, 2.5f}, {128, 1, 1, 3.5f},
+    {64, 4, 4, 1.0f},  {64, 3, 4, 1.0f},  {64, 2, 1, 1.25f}, {64, 1, 1, 2.2f},
 };
 // One more pass over the keys of a (sequence, KV head), in padded-row units.
 constexpr float kRereadRows = 60.f;
