@@ -159,6 +159,46 @@ def summarize_counters(fetch_csv, write_csv):
     print(json.dumps(out, indent=1))
 
 
+def step_distribution(dev, k, stream):
+    """Median, 10th and 90th percentile of k single verification steps (ms)."""
+    import numpy as np
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        dev.verify_step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"median_ms": round(float(np.median(t)), 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+            "p90_ms": round(float(np.percentile(t, 90)), 5), "steps": k}
+
+
+def rotated_steps(dev, cfg, k, stream):
+    """ms per step over k steps alternating between this input set and a second
+    one of the same shape (another seed): every step's inputs were last touched
+    two steps earlier, after 2.7 GB of other traffic."""
+    import torch
+    from eagle_tree_verification_attn_amd.problem import DeviceProblem
+    from synth import make_instance
+    other = DeviceProblem(make_instance(cfg, 1), device="cuda:0")
+    devs = (dev, other)
+    for i in range(4):
+        devs[i % 2].verify_step()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(k):
+        devs[i % 2].verify_step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del other
+    torch.cuda.empty_cache()
+    return a.elapsed_time(b) / k
+
+
 def time_commit(dev, inst, res, n, stream):
     """sv_commit_accepted on the step's accept results, into destination caches
     of L_max = prefix + T_max; returns (ms per launch, bytes moved)."""
@@ -306,6 +346,12 @@ def main():
     print(f"bench: {args.steps} steps, {ms_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})",
           file=sys.stderr, flush=True)
 
+    # the distribution of single steps (events around each step, after the
+    # timed region), and steps alternating over two input sets so that no step
+    # finds the previous step's inputs in the caches
+    per_step = step_distribution(dev, args.steps, stream)
+    rotated_ms = rotated_steps(dev, cfg, args.steps, stream)
+
     n = max(10, args.steps)
     mask_ms = time_launches(dev.mask_build, n, stream)
     attn_ms = time_launches(dev.tree_attn, n, stream)
@@ -321,6 +367,9 @@ def main():
     attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
     acc_bytes = accept_bytes(inst, res)
     acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
+    sz_logit = 2 if inst.logit_dtype == "bf16" else 4
+    every_row_bytes = float(sz_logit * inst.V * int(inst.num_nodes.sum()))
+    every_row_ms = every_row_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
     traffic = counters_traffic()
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -352,6 +401,9 @@ def main():
         "cpu_baseline": cpu,
         "kernels_ms": {"tree_mask_build": round(mask_ms, 5), "tree_attn": round(attn_ms, 5),
                        "spec_accept": round(acc_ms, 5)},
+        "per_step": per_step,
+        "rotated_inputs": {"ms_per_step": round(rotated_ms, 5), "steps_per_s": round(1e3 / rotated_ms, 2),
+                           "note": "two input sets alternating, so no step reuses cached inputs"},
         "commit_accepted": {"ms": round(commit_ms, 5), "bytes": commit_bytes,
                             "note": "after the step, not part of it"},
         "eagle2_build": e2,
@@ -360,7 +412,13 @@ def main():
                                               "frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
                          "tree_spec_accept": {"algorithmic_bytes": acc_bytes,
                                               "GB_s": round(acc_gbs, 1),
-                                              "frac": round(acc_gbs / HBM_PEAK_GBS, 4)}},
+                                              "frac": round(acc_gbs / HBM_PEAK_GBS, 4),
+                                              # the same results from a softmax over every tree
+                                              # row would read each logits row once: that
+                                              # read's time at peak, against this walk's time
+                                              "every_row_once_bytes": every_row_bytes,
+                                              "every_row_once_roofline_ms": round(every_row_ms, 5),
+                                              "walk_ms_vs_that_roofline": round(acc_ms / every_row_ms, 4)}},
         "emitted_tokens_per_seq": round(float(np.mean(res["out_count"])), 3),
         "vocab_passes_per_seq": round(float(np.mean(res["out_passes"])), 3),
     }
