@@ -26,7 +26,8 @@ SV_SIB_WITHOUT_REPLACEMENT, SV_SIB_IID = 0, 1
 
 EXPORTS = ["sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step",
            "sv_commit_accepted", "sv_workspace_bytes", "sv_status_string", "sv_last_error",
-           "sv_eagle2_state_bytes", "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish"]
+           "sv_eagle2_state_bytes", "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish",
+           "sv_draft_head"]
 
 
 class SvTree(ctypes.Structure):
@@ -54,6 +55,13 @@ class SvAcceptArgs(ctypes.Structure):
 class SvEagle2Cfg(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("V", ctypes.c_int32), ("k", ctypes.c_int32), ("depth", ctypes.c_int32),
                 ("m", ctypes.c_int32)]
+
+
+class SvHeadArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("d", ctypes.c_int32), ("r", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("tile", ctypes.c_int32), ("k_tile", ctypes.c_int32), ("h", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("A_sh", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("W", ctypes.c_void_p), ("u", ctypes.c_void_p),
+                ("cand_ids", ctypes.c_void_p), ("cand_logits", ctypes.c_void_p)]
 
 
 class SvCommitArgs(ctypes.Structure):
@@ -102,6 +110,7 @@ def lib():
         L.sv_eagle2_finish.argtypes = [P(SvEagle2Cfg), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]
+        L.sv_draft_head.argtypes = [P(SvHeadArgs), ctypes.c_void_p]
         L.sv_workspace_bytes.argtypes = [P(SvTree), P(SvAttnArgs), P(SvAcceptArgs)]
         L.sv_workspace_bytes.restype = ctypes.c_size_t
         L.sv_status_string.argtypes = [ctypes.c_int32]
@@ -109,7 +118,7 @@ def lib():
         L.sv_last_error.argtypes = []
         L.sv_last_error.restype = ctypes.c_char_p
         for f in ("sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_commit_accepted",
-                  "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish"):
+                  "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish", "sv_draft_head"):
             getattr(L, f).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -244,6 +253,21 @@ def sv_eagle2_finish(cfg, state, parent, tokens, num_nodes, q_row, status, strea
     return _check(lib().sv_eagle2_finish(ctypes.byref(cfg), _ptr(state), _nbytes(state), _ptr(parent), _ptr(tokens),
                                          _ptr(num_nodes), _ptr(q_row), _ptr(status), _stream(stream)),
                   "sv_eagle2_finish", raise_on_error)
+
+
+def make_head_args(h, B, A_sh, perm, W, u, cand_ids, cand_logits, tile, k_tile):
+    """sv_head_args: h [N][d], B [r][d], A_sh [n][r], W [n][d] bf16; perm [n] int32; outputs u [N][r] bf16,
+    cand_ids int32 / cand_logits fp32 [N][ceil(n / tile) * k_tile]."""
+    N, d = int(h.shape[0]), int(h.shape[1])
+    r, n = int(B.shape[0]), int(A_sh.shape[0])
+    a = SvHeadArgs(N, d, r, n, int(tile), int(k_tile), _ptr(h), _ptr(B), _ptr(A_sh), _ptr(perm), _ptr(W), _ptr(u),
+                   _ptr(cand_ids), _ptr(cand_logits))
+    a._keep = (h, B, A_sh, perm, W, u, cand_ids, cand_logits)
+    return a
+
+
+def sv_draft_head(args, stream=None, raise_on_error=True):
+    return _check(lib().sv_draft_head(ctypes.byref(args), _stream(stream)), "sv_draft_head", raise_on_error)
 
 
 def sv_workspace_bytes(tree, attn=None, acc=None):

@@ -1,0 +1,215 @@
+// Two-stage draft LM head ([EAGLE-4 blog], sections "EAGLE Efficient LM
+// Head", "A training-free version: Freq-aware SVD", "A variant based on Local
+// Top-k"): a low-rank head A B scores the whole vocabulary cheaply, each tile
+// of the shuffled vocabulary keeps its own best candidates while the scores
+// are still on chip, and the full head W recomputes exact logits for the
+// candidates only.
+//
+//   k_head_u       u = B h, one 16 x 16 (rank x position) MFMA tile per
+//                  workgroup; the four waves split the hidden dim and their
+//                  partial tiles are summed in LDS in a fixed order; float32
+//                  sums rounded to bf16 (the operand of the next stage).
+//   k_head_topk    one workgroup per vocabulary tile: scores^T = A_tile u^T on
+//                  MFMA into LDS (never written to HBM), then per position the
+//                  k_tile best rows by wave argmax rounds over 64-bit keys
+//                  (order-preserving score bits above the complement of the
+//                  row), written as token ids through the shuffle.
+//   k_head_logits  one wave per (position, candidate): the candidate's row of
+//                  W gathered once and dotted with h in float32.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16): lane l holds A[l % 16][8 (l / 16)
+// .. + 7] and B[8 (l / 16) .. + 7][l % 16], and receives D[4 (l / 16) + i][l %
+// 16], i = 0..3.  Both operands are rows of row-major tensors read as 16-byte
+// runs, so they load straight from global memory.
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int kHeadMaxK = 8;      // candidates per tile
+constexpr int kHeadTileMax = 256; // vocabulary rows per tile
+
+struct HeadParams {
+  int N, d, r, n, tile, k_tile, n_tiles;
+  const __bf16* h;
+  const __bf16* B;
+  const __bf16* A;
+  const int32_t* perm;
+  const __bf16* W;
+  __bf16* u;
+  int32_t* cand_ids;
+  float* cand_logits;
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline bf16x8 load8(const __bf16* p) { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p)); }
+
+__device__ inline uint16_t bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// An order-preserving unsigned image of a float32 (larger float -> larger).
+__device__ inline uint32_t sortable(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ inline uint64_t wave_max64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- stage 1
+// grid (r / 16, ceil(N / 16)); 4 waves, each over a quarter of the hidden dim.
+__global__ __launch_bounds__(256) void k_head_u(HeadParams p) {
+  __shared__ f32x4 part_s[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = blockIdx.x * 16, n0 = blockIdx.y * 16;
+  const int row = r0 + (lane & 15);              // rank row of the A operand
+  const int pos = n0 + (lane & 15);              // position of the B operand
+  const int kg = lane >> 4;
+  const bool pos_ok = pos < p.N;
+  const int steps = p.d / 32;
+  const int per = (steps + 3) / 4;
+  const int s0 = wave * per, s1 = min(steps, s0 + per);
+  const __bf16* brow = p.B + (size_t)row * p.d + 8 * kg;
+  const __bf16* hrow = p.h + (size_t)(pos_ok ? pos : 0) * p.d + 8 * kg;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8 zero = {};
+  for (int s = s0; s < s1; ++s) {
+    const bf16x8 a = load8(brow + 32 * s);
+    const bf16x8 b = pos_ok ? load8(hrow + 32 * s) : zero;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  part_s[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    const f32x4 t = ((part_s[0][lane] + part_s[1][lane]) + part_s[2][lane]) + part_s[3][lane];
+    if (pos_ok) {
+      uint16_t* u = reinterpret_cast<uint16_t*>(p.u) + (size_t)pos * p.r + r0 + 4 * kg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = bf16_rne(t[i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- stage 2
+// grid (n_tiles, ceil(N / 16)); 4 waves; wave w scores rows 16 q + w*16 ...
+__global__ __launch_bounds__(256) void k_head_topk(HeadParams p) {
+  __shared__ float sc_s[kHeadTileMax][17];      // [row in tile][position], padded
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+  const int n0 = blockIdx.y * 16;
+  const int lo = t * p.tile;
+  const int rows = min(p.tile, p.n - lo);
+  const int kg = lane >> 4;
+  const int pos = n0 + (lane & 15);
+  const bool pos_ok = pos < p.N;
+  const int ksteps = p.r / 32;
+  const __bf16* urow = p.u + (size_t)(pos_ok ? pos : 0) * p.r + 8 * kg;
+  const bf16x8 zero = {};
+  // 16-row blocks of the tile, round robin over the waves
+  for (int rb = wave; rb * 16 < rows; rb += 4) {
+    const int row = rb * 16 + (lane & 15);
+    const bool row_ok = row < rows;
+    const __bf16* arow = p.A + (size_t)(lo + (row_ok ? row : 0)) * p.r + 8 * kg;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ksteps; ++s) {
+      const bf16x8 a = row_ok ? load8(arow + 32 * s) : zero;
+      const bf16x8 b = pos_ok ? load8(urow + 32 * s) : zero;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc_s[rb * 16 + 4 * kg + i][lane & 15] = acc[i];
+  }
+  __syncthreads();
+  // per position: the k_tile best rows (score descending, then row ascending)
+  const int npos = min(16, p.N - n0);
+  const int kk = min(p.k_tile, rows);
+  for (int q = wave; q < npos; q += 4) {
+    const int i = n0 + q;
+    uint64_t key[kHeadTileMax / 64];
+#pragma unroll
+    for (int j = 0; j < kHeadTileMax / 64; ++j) {
+      const int row = lane + 64 * j;
+      key[j] = row < rows ? (((uint64_t)sortable(sc_s[row][q]) << 32) | (uint32_t)~row) : 0;
+    }
+    int32_t* ids = p.cand_ids + (size_t)i * p.n_tiles * p.k_tile + (size_t)t * p.k_tile;
+    for (int c = 0; c < p.k_tile; ++c) {
+      int id = -1;
+      if (c < kk) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int j = 0; j < kHeadTileMax / 64; ++j) m = key[j] > m ? key[j] : m;
+        const uint64_t best = wave_max64(m);
+        const int row = (int)~(uint32_t)best;
+#pragma unroll
+        for (int j = 0; j < kHeadTileMax / 64; ++j) key[j] = key[j] == best ? 0 : key[j];
+        id = p.perm[lo + row];
+      }
+      if (lane == 0) ids[c] = id;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- stage 3
+// one wave per (position, candidate); 4 waves per workgroup.
+__global__ __launch_bounds__(256) void k_head_logits(HeadParams p) {
+  const int lane = threadIdx.x & 63;
+  const size_t C = (size_t)p.n_tiles * p.k_tile;
+  const size_t job = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (job >= (size_t)p.N * C) return;
+  const int i = (int)(job / C);
+  const int id = p.cand_ids[job];
+  float acc = 0.f;
+  if (id >= 0 && id < p.n) {
+    const __bf16* w = p.W + (size_t)id * p.d;
+    const __bf16* h = p.h + (size_t)i * p.d;
+    for (int k = 8 * lane; k < p.d; k += 512) {
+      const bf16x8 a = load8(w + k);
+      const bf16x8 b = load8(h + k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) p.cand_logits[job] = id >= 0 ? acc : 0.f;
+}
+
+// ---------------------------------------------------------------- launch
+sv_status launch_draft_head(const sv_head_args* a, hipStream_t s) {
+  HeadParams p{};
+  p.N = a->N; p.d = a->d; p.r = a->r; p.n = a->n; p.tile = a->tile; p.k_tile = a->k_tile;
+  p.n_tiles = (a->n + a->tile - 1) / a->tile;
+  p.h = static_cast<const __bf16*>(a->h);
+  p.B = static_cast<const __bf16*>(a->B);
+  p.A = static_cast<const __bf16*>(a->A_sh);
+  p.perm = a->perm;
+  p.W = static_cast<const __bf16*>(a->W);
+  p.u = static_cast<__bf16*>(a->u);
+  p.cand_ids = a->cand_ids;
+  p.cand_logits = a->cand_logits;
+  if (p.N == 0) return SV_OK;
+  const int pos_tiles = (p.N + 15) / 16;
+  hipLaunchKernelGGL(k_head_u, dim3(p.r / 16, pos_tiles), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) { set_error("draft head stage 1 launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  hipLaunchKernelGGL(k_head_topk, dim3(p.n_tiles, pos_tiles), dim3(256), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) { set_error("draft head stage 2 launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  const size_t jobs = (size_t)p.N * p.n_tiles * p.k_tile;
+  hipLaunchKernelGGL(k_head_logits, dim3((unsigned)((jobs + 3) / 4)), dim3(256), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) { set_error("draft head stage 3 launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  return SV_OK;
+}
+
+}  // namespace sv

@@ -274,6 +274,34 @@ sv_status sv_eagle2_finish(const sv_eagle2_cfg* c, const void* state, size_t sta
   return launch_eagle2_finish(c, state, parent, tokens, num_nodes, q_row, status, (hipStream_t)stream);
 }
 
+sv_status sv_draft_head(const sv_head_args* a, void* stream) {
+  clear_error();
+  if (!a) { set_error("draft-head args are NULL"); return SV_E_NULL; }
+  if (a->N < 0 || a->d < 32 || a->d % 32 || a->r < 32 || a->r % 32 || a->n < 1) {
+    set_error("draft head N=%d d=%d r=%d n=%d (need d, r multiples of 32)", a->N, a->d, a->r, a->n);
+    return SV_E_SHAPE;
+  }
+  if (a->tile < 16 || a->tile > 256 || a->tile % 16 || a->k_tile < 1 || a->k_tile > 8 || a->k_tile > a->tile) {
+    set_error("draft head tile=%d k_tile=%d (tile: multiple of 16 in [16, 256]; k_tile 1..8)", a->tile, a->k_tile);
+    return SV_E_UNSUPPORTED;
+  }
+  if (a->r > 2048) { set_error("draft head r=%d > 2048", a->r); return SV_E_UNSUPPORTED; }
+  const long n_tiles = (a->n + (long)a->tile - 1) / a->tile;
+  if ((long)a->N * n_tiles * a->k_tile > 0x7FFFFFFFL || (a->N + 15) / 16 > 65535) {
+    set_error("draft head N=%d too large", a->N);
+    return SV_E_UNSUPPORTED;
+  }
+  if (a->N == 0) return SV_OK;
+  if (!a->h || !a->B || !a->A_sh || !a->perm || !a->W || !a->u || !a->cand_ids || !a->cand_logits) {
+    set_error("draft head h/B/A_sh/perm/W/u/cand_ids/cand_logits is NULL");
+    return SV_E_NULL;
+  }
+  const void* ptrs[] = {a->h, a->B, a->A_sh, a->W, a->u};
+  for (const void* q : ptrs)
+    if (!aligned(q, 16)) { set_error("draft head tensors must be 16-byte aligned"); return SV_E_UNSUPPORTED; }
+  return launch_draft_head(a, (hipStream_t)stream);
+}
+
 size_t sv_workspace_bytes(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc) {
   clear_error();
   // sizing reads only the scalar fields: pointers may be NULL here

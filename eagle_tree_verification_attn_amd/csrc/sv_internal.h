@@ -75,6 +75,9 @@ sv_status launch_eagle2_expand(const sv_eagle2_cfg* c, void* state, int step, co
 sv_status launch_eagle2_finish(const sv_eagle2_cfg* c, const void* state, int32_t* parent, int32_t* tokens,
                                int32_t* num_nodes, int32_t* q_row, int32_t* status, hipStream_t s);
 
+// ---------------------------------------------------------------- draft head
+sv_status launch_draft_head(const sv_head_args* a, hipStream_t s);
+
 // ---------------------------------------------------------------- mask
 sv_status launch_mask(const sv_tree* t, uint64_t* anc, int32_t* depth, int32_t* tree_status,
                       hipStream_t s);

@@ -286,6 +286,43 @@ sv_status sv_eagle2_finish(const sv_eagle2_cfg* c, const void* state, size_t sta
                            int32_t* parent, int32_t* tokens, int32_t* num_nodes, int32_t* q_row,
                            int32_t* status, void* stream);
 
+/* ---------------------------------------------------------------- draft head
+ * Two-stage draft LM head ([EAGLE-4 blog], sections "EAGLE Efficient LM
+ * Head", "A training-free version: Freq-aware SVD", "A variant based on Local
+ * Top-k").  Stage 1: u = B h.  Stage 2: approximate scores A u over a
+ * shuffled vocabulary, and in each tile of `tile` consecutive shuffled rows
+ * the k_tile best per position are kept as candidates (the scores never leave
+ * the chip).  Stage 3: exact logits W[id] . h for the candidates only.  A and
+ * B are low-rank factors of W made offline (for example the page's
+ * frequency-weighted truncated SVD, A = F^(-1/2) U_r S_r, B = V_r^T with
+ * F^(1/2) W = U S V^T); A's rows are stored in the shuffled order and perm
+ * maps a shuffled row to its token id.
+ * Precision: bf16 inputs, float32 accumulation; u is stored as bf16 (rounded
+ * to nearest even); within a tile, equal scores go to the lower shuffled row.
+ * Candidates of position i are cand_ids[i][t * k_tile + c] for tile t and
+ * rank c; a last tile shorter than k_tile pads with id -1 and logit 0. */
+typedef struct {
+  int32_t N;                /* draft positions (rows of h), >= 0                        */
+  int32_t d;                /* hidden size, a multiple of 32                            */
+  int32_t r;                /* rank of the factors, a multiple of 32, <= 2048           */
+  int32_t n;                /* vocabulary size, >= 1                                    */
+  int32_t tile;             /* shuffled rows per tile, a multiple of 16 in [16, 256]    */
+  int32_t k_tile;           /* candidates kept per tile, 1..8, <= tile                  */
+  const void* h;            /* [N][d] bf16 hidden states                                 */
+  const void* B;            /* [r][d] bf16                                               */
+  const void* A_sh;         /* [n][r] bf16, rows in shuffled order                       */
+  const int32_t* perm;      /* [n] token id of each shuffled row                         */
+  const void* W;            /* [n][d] bf16 full head, rows in token order                */
+  void* u;                  /* [N][r] bf16 out: stage 1                                  */
+  int32_t* cand_ids;        /* [N][ceil(n / tile) * k_tile] out: candidate token ids     */
+  float* cand_logits;       /* [N][ceil(n / tile) * k_tile] out: their exact logits      */
+} sv_head_args;
+
+/* Runs the three stages in stream order.  All arrays are device memory,
+ * 16-byte aligned (h, B, A_sh, W, u).  Inputs are trusted to be finite and
+ * perm to be a permutation of [0, n); ids outside [0, n) give logit 0. */
+sv_status sv_draft_head(const sv_head_args* a, void* stream);
+
 /* Workspace bytes needed by sv_tree_attn (attn != NULL), sv_spec_accept
  * (acc != NULL) or both (the maximum).  Host only; reads only the scalar
  * fields of the structs.  Returns 0 on invalid sizes (see sv_last_error). */

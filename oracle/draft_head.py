@@ -102,13 +102,12 @@ def stage3(h, W, perm, cand_pos):
     """Exact logits of the candidates: W[perm[pos]] . h (float64 sums of the
     stored values); -1 slots give id -1 and logit 0."""
     h = np.asarray(h, dtype=np.float64)
-    W = np.asarray(W, dtype=np.float64)
     perm = np.asarray(perm)
     ids = np.where(cand_pos >= 0, perm[np.maximum(cand_pos, 0)], -1)
     logits = np.zeros(cand_pos.shape, dtype=np.float64)
     for i in range(cand_pos.shape[0]):
         ok = ids[i] >= 0
-        logits[i, ok] = W[ids[i, ok]] @ h[i]
+        logits[i, ok] = np.asarray(W[ids[i, ok]], dtype=np.float64) @ h[i]   # only the gathered rows
     return ids, logits
 
 

@@ -9,8 +9,8 @@ drafter's outputs, so producing them belongs here (a synthetic drafter).
 """
 from .configs import CONFIGS, config_by_name, small_spec
 from .gen import (Instance, make_instance, bf16_bits_from_f32, f32_from_bf16_bits,
-                  tree_from_widths, random_tree_widths, make_draft_rows)
+                  tree_from_widths, random_tree_widths, make_draft_rows, make_head_inputs)
 
 __all__ = ["CONFIGS", "config_by_name", "small_spec", "Instance", "make_instance",
            "bf16_bits_from_f32", "f32_from_bf16_bits", "tree_from_widths",
-           "random_tree_widths", "make_draft_rows"]
+           "random_tree_widths", "make_draft_rows", "make_head_inputs"]

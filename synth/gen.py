@@ -287,3 +287,26 @@ def make_draft_rows(B, k, depth, V, seed=0, draft_std=3.0, tie_step=None, cfg_id
             p = np.floor(p / tie_step) * tie_step
         out.append(p.astype(np.float32))
     return out
+
+
+def make_head_inputs(N, d, r, n, seed=0, quantized=True, with_W=True, cfg_id=910):
+    """Inputs of the two-stage draft head: h [N][d], B [r][d], A_sh [n][r],
+    W [n][d] as bf16 bit patterns (uint16) and a shuffle perm [n] (int32).
+    With ``quantized`` every value is a multiple of 1/8 in [-1, 1], so float32
+    sums of their products are exact (and so is u = B h at these sizes);
+    otherwise N(0, 1) for h and N(0, 1/d), N(0, 1/r) for the factors and W.
+    Seeded by ``SeedSequence([cfg_id, seed])``: one Philox stream per tensor."""
+    ss = np.random.SeedSequence([cfg_id, int(seed)]).spawn(5)
+    g = [np.random.Generator(np.random.Philox(x)) for x in ss]
+
+    def draw(rng, shape, std):
+        if quantized:
+            return (rng.integers(-8, 9, size=shape) / 8.0).astype(np.float32)
+        return (rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+    h = bf16_bits_from_f32(draw(g[0], (N, d), 1.0))
+    B = bf16_bits_from_f32(draw(g[1], (r, d), 1.0 / np.sqrt(d)))
+    A_sh = bf16_bits_from_f32(draw(g[2], (n, r), 1.0 / np.sqrt(r)))
+    perm = g[3].permutation(n).astype(np.int32)
+    W = bf16_bits_from_f32(draw(g[4], (n, d), 1.0 / np.sqrt(d))) if with_W else None
+    return dict(h=h, B=B, A_sh=A_sh, perm=perm, W=W)

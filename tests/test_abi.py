@@ -174,3 +174,24 @@ def test_plain_c_client_builds_and_passes(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "passed" in r.stdout
+
+
+def test_draft_head_host_checks():
+    L = sv.lib()
+    fake = 0x100000
+
+    def args(**kw):
+        a = sv.SvHeadArgs(8, 8192, 256, 128256, 256, 2, fake, fake, fake, fake, fake, fake, fake, fake)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+    assert L.sv_draft_head(None, None) == sv.SV_E_NULL
+    for bad, code in ((dict(d=100), sv.SV_E_SHAPE), (dict(r=48), sv.SV_E_SHAPE), (dict(n=0), sv.SV_E_SHAPE),
+                      (dict(N=-1), sv.SV_E_SHAPE), (dict(tile=24), sv.SV_E_UNSUPPORTED),
+                      (dict(tile=512), sv.SV_E_UNSUPPORTED), (dict(k_tile=9), sv.SV_E_UNSUPPORTED),
+                      (dict(k_tile=0), sv.SV_E_UNSUPPORTED), (dict(r=4096), sv.SV_E_UNSUPPORTED),
+                      (dict(W=None), sv.SV_E_NULL), (dict(h=fake + 8), sv.SV_E_UNSUPPORTED)):
+        a = args(**bad)
+        assert L.sv_draft_head(ctypes.byref(a), None) == code, bad
+        assert sv.sv_last_error()
+    assert L.sv_draft_head(ctypes.byref(args(N=0, h=None, W=None)), None) == sv.SV_OK
