@@ -248,6 +248,40 @@ def time_eagle2(inst, n, stream):
             "sequences_ok": ok, "note": "before the step, not part of it"}
 
 
+def time_draft_head(inst, n_launch, stream):
+    """The two-stage draft LM head for one sequence's drafter step: 8 positions,
+    hidden 8192 (the 70B shape), rank 256, the batch's vocabulary, tiles of
+    256 shuffled rows keeping 2 candidates each; inputs made on the device.
+    Returns the time, the algorithmic bytes (B and A once, the candidates'
+    rows of W) and, for context, the time a full head would need to read W
+    once at peak bandwidth."""
+    import torch
+    import eagle_tree_verification_attn_amd as sv
+    N, d, r, n, tile, k_tile = 8, 8192, 256, inst.V, 256, 2
+    g = torch.Generator(device="cuda").manual_seed(13)
+    bf = torch.bfloat16
+    h = torch.randn((N, d), generator=g, device="cuda").to(bf)
+    B = (torch.randn((r, d), generator=g, device="cuda") / d ** 0.5).to(bf)
+    A = (torch.randn((n, r), generator=g, device="cuda") / r ** 0.5).to(bf)
+    W = (torch.randn((n, d), generator=g, device="cuda") / d ** 0.5).to(bf)
+    perm = torch.randperm(n, generator=g, device="cuda").to(torch.int32)
+    C = -(-n // tile) * k_tile
+    u = torch.empty((N, r), dtype=bf, device="cuda")
+    ids = torch.empty((N, C), dtype=torch.int32, device="cuda")
+    logits = torch.empty((N, C), dtype=torch.float32, device="cuda")
+    args = sv.make_head_args(h, B, A, perm, W, u, ids, logits, tile, k_tile)
+    for _ in range(3):
+        sv.sv_draft_head(args, stream)
+    ms = time_launches(lambda: sv.sv_draft_head(args, stream), n_launch, stream)
+    nbytes = float(2 * (r * d + n * r + N * C * d) + 4 * n + 8 * N * C)
+    full_ms = 2.0 * n * d / (HBM_PEAK_GBS * 1e9) * 1e3
+    del W, A
+    return {"workload": f"draft_head_n{N}_d{d}_r{r}_v{n}_tile{tile}_k{k_tile}", "ms": round(ms, 5),
+            "bytes": nbytes, "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "full_head_read_roofline_ms": round(full_ms, 5), "note": "drafter side, not part of the step"}
+
+
 def cpu_baseline(inst, seconds):
     """The oracle on a bounded sample: whole sequences (attention for all heads,
     target softmax and walk), scaled to steps/s of the full batch."""
@@ -361,6 +395,7 @@ def main():
     # room after the prefix, so the step's own caches stay as they are
     commit_ms, commit_bytes = time_commit(dev, inst, res, n, stream)
     e2 = time_eagle2(inst, n, stream)
+    head = time_draft_head(inst, n, stream)
     flops, attn_bytes = algorithmic_work(inst)
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
@@ -407,6 +442,7 @@ def main():
         "commit_accepted": {"ms": round(commit_ms, 5), "bytes": commit_bytes,
                             "note": "after the step, not part of it"},
         "eagle2_build": e2,
+        "draft_head": head,
         "hbm_roofline": {"tree_attn_verify": {"algorithmic_bytes": attn_bytes,
                                               "GB_s": round(attn_gbs, 1),
                                               "frac": round(attn_gbs / HBM_PEAK_GBS, 4)},

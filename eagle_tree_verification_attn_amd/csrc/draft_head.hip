@@ -5,10 +5,11 @@
 // are still on chip, and the full head W recomputes exact logits for the
 // candidates only.
 //
-//   k_head_u       u = B h, one 16 x 16 (rank x position) MFMA tile per
-//                  workgroup; the four waves split the hidden dim and their
-//                  partial tiles are summed in LDS in a fixed order; float32
-//                  sums rounded to bf16 (the operand of the next stage).
+//   k_head_u       u = B h: one 16 x 16 (rank x position) MFMA tile per
+//                  workgroup of 16 waves, each over a sixteenth of the hidden
+//                  dim with 8 k-steps of loads in flight; the waves' partial
+//                  tiles are summed in LDS in a fixed order and rounded to
+//                  bf16 (the operand of the next stage).
 //   k_head_topk    one workgroup per vocabulary tile: scores^T = A_tile u^T on
 //                  MFMA into LDS (never written to HBM), then per position the
 //                  k_tile best rows by wave argmax rounds over 64-bit keys
@@ -27,6 +28,9 @@ namespace sv {
 
 constexpr int kHeadMaxK = 8;      // candidates per tile
 constexpr int kHeadTileMax = 256; // vocabulary rows per tile
+
+constexpr int kUWaves = 16;       // stage-1 waves per workgroup
+constexpr int kTopkWaves = 8;     // stage-2 waves per workgroup
 
 struct HeadParams {
   int N, d, r, n, tile, k_tile, n_tiles;
@@ -67,42 +71,50 @@ __device__ inline uint64_t wave_max64(uint64_t v) {
 }
 
 // ---------------------------------------------------------------- stage 1
-// grid (r / 16, ceil(N / 16)); 4 waves, each over a quarter of the hidden dim.
-__global__ __launch_bounds__(256) void k_head_u(HeadParams p) {
-  __shared__ f32x4 part_s[4][64];
+// grid (r / 16, ceil(N / 16)); wave w sums k-steps [w ksteps / 16, (w + 1) ksteps / 16).
+__global__ __launch_bounds__(64 * kUWaves) void k_head_u(HeadParams p) {
+  __shared__ f32x4 part_s[kUWaves][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = blockIdx.x * 16, n0 = blockIdx.y * 16;
   const int row = r0 + (lane & 15);              // rank row of the A operand
   const int pos = n0 + (lane & 15);              // position of the B operand
   const int kg = lane >> 4;
   const bool pos_ok = pos < p.N;
-  const int steps = p.d / 32;
-  const int per = (steps + 3) / 4;
-  const int s0 = wave * per, s1 = min(steps, s0 + per);
+  const int ksteps = p.d / 32;
+  const int s_begin = (int)((long)ksteps * wave / kUWaves);
+  const int s_end = (int)((long)ksteps * (wave + 1) / kUWaves);
   const __bf16* brow = p.B + (size_t)row * p.d + 8 * kg;
   const __bf16* hrow = p.h + (size_t)(pos_ok ? pos : 0) * p.d + 8 * kg;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero = {};
-  for (int s = s0; s < s1; ++s) {
-    const bf16x8 a = load8(brow + 32 * s);
-    const bf16x8 b = pos_ok ? load8(hrow + 32 * s) : zero;
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = s_begin; s0 < s_end; s0 += 8) {
+    bf16x8 a[8], b[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bool ok = s0 + s < s_end;
+      a[s] = ok ? load8(brow + 32 * (s0 + s)) : zero;
+      b[s] = ok && pos_ok ? load8(hrow + 32 * (s0 + s)) : zero;
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s0 + s < s_end) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
   }
   part_s[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0) {
-    const f32x4 t = ((part_s[0][lane] + part_s[1][lane]) + part_s[2][lane]) + part_s[3][lane];
-    if (pos_ok) {
-      uint16_t* u = reinterpret_cast<uint16_t*>(p.u) + (size_t)pos * p.r + r0 + 4 * kg;
+  if (wave == 0 && pos_ok) {
+    f32x4 t = part_s[0][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = bf16_rne(t[i]);
-    }
+    for (int w = 1; w < kUWaves; ++w) t += part_s[w][lane];
+    uint16_t* u = reinterpret_cast<uint16_t*>(p.u) + (size_t)pos * p.r + r0 + 4 * kg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = bf16_rne(t[i]);
   }
 }
 
 // ---------------------------------------------------------------- stage 2
-// grid (n_tiles, ceil(N / 16)); 4 waves; wave w scores rows 16 q + w*16 ...
-__global__ __launch_bounds__(256) void k_head_topk(HeadParams p) {
+// grid (n_tiles, ceil(N / 16)); 8 waves; wave w scores the tile's 16-row
+// blocks w, w + 8, ...
+__global__ __launch_bounds__(64 * kTopkWaves) void k_head_topk(HeadParams p) {
   __shared__ float sc_s[kHeadTileMax][17];      // [row in tile][position], padded
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
@@ -116,15 +128,22 @@ __global__ __launch_bounds__(256) void k_head_topk(HeadParams p) {
   const __bf16* urow = p.u + (size_t)(pos_ok ? pos : 0) * p.r + 8 * kg;
   const bf16x8 zero = {};
   // 16-row blocks of the tile, round robin over the waves
-  for (int rb = wave; rb * 16 < rows; rb += 4) {
+  for (int rb = wave; rb * 16 < rows; rb += kTopkWaves) {
     const int row = rb * 16 + (lane & 15);
     const bool row_ok = row < rows;
     const __bf16* arow = p.A + (size_t)(lo + (row_ok ? row : 0)) * p.r + 8 * kg;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ksteps; ++s) {
-      const bf16x8 a = row_ok ? load8(arow + 32 * s) : zero;
-      const bf16x8 b = pos_ok ? load8(urow + 32 * s) : zero;
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    for (int s0 = 0; s0 < ksteps; s0 += 8) {
+      bf16x8 a[8], b[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bool ok = s0 + s < ksteps;
+        a[s] = ok && row_ok ? load8(arow + 32 * (s0 + s)) : zero;
+        b[s] = ok && pos_ok ? load8(urow + 32 * (s0 + s)) : zero;
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s0 + s < ksteps) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc_s[rb * 16 + 4 * kg + i][lane & 15] = acc[i];
@@ -133,7 +152,7 @@ __global__ __launch_bounds__(256) void k_head_topk(HeadParams p) {
   // per position: the k_tile best rows (score descending, then row ascending)
   const int npos = min(16, p.N - n0);
   const int kk = min(p.k_tile, rows);
-  for (int q = wave; q < npos; q += 4) {
+  for (int q = wave; q < npos; q += kTopkWaves) {
     const int i = n0 + q;
     uint64_t key[kHeadTileMax / 64];
 #pragma unroll
@@ -199,10 +218,10 @@ sv_status launch_draft_head(const sv_head_args* a, hipStream_t s) {
   p.cand_logits = a->cand_logits;
   if (p.N == 0) return SV_OK;
   const int pos_tiles = (p.N + 15) / 16;
-  hipLaunchKernelGGL(k_head_u, dim3(p.r / 16, pos_tiles), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_head_u, dim3(p.r / 16, pos_tiles), dim3(64 * kUWaves), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) { set_error("draft head stage 1 launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
-  hipLaunchKernelGGL(k_head_topk, dim3(p.n_tiles, pos_tiles), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_head_topk, dim3(p.n_tiles, pos_tiles), dim3(64 * kTopkWaves), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) { set_error("draft head stage 2 launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
   const size_t jobs = (size_t)p.N * p.n_tiles * p.k_tile;

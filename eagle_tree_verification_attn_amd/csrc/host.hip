@@ -274,8 +274,9 @@ sv_status sv_eagle2_finish(const sv_eagle2_cfg* c, const void* state, size_t sta
   return launch_eagle2_finish(c, state, parent, tokens, num_nodes, q_row, status, (hipStream_t)stream);
 }
 
-sv_status sv_draft_head(const sv_head_args* a, void* stream) {
-  clear_error();
+namespace sv {
+namespace {
+sv_status check_head(const sv_head_args* a) {
   if (!a) { set_error("draft-head args are NULL"); return SV_E_NULL; }
   if (a->N < 0 || a->d < 32 || a->d % 32 || a->r < 32 || a->r % 32 || a->n < 1) {
     set_error("draft head N=%d d=%d r=%d n=%d (need d, r multiples of 32)", a->N, a->d, a->r, a->n);
@@ -291,6 +292,15 @@ sv_status sv_draft_head(const sv_head_args* a, void* stream) {
     set_error("draft head N=%d too large", a->N);
     return SV_E_UNSUPPORTED;
   }
+  return SV_OK;
+}
+}  // namespace
+}  // namespace sv
+
+sv_status sv_draft_head(const sv_head_args* a, void* stream) {
+  clear_error();
+  sv_status st;
+  if ((st = check_head(a))) return st;
   if (a->N == 0) return SV_OK;
   if (!a->h || !a->B || !a->A_sh || !a->perm || !a->W || !a->u || !a->cand_ids || !a->cand_logits) {
     set_error("draft head h/B/A_sh/perm/W/u/cand_ids/cand_logits is NULL");

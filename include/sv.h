@@ -318,9 +318,10 @@ typedef struct {
   float* cand_logits;       /* [N][ceil(n / tile) * k_tile] out: their exact logits      */
 } sv_head_args;
 
-/* Runs the three stages in stream order.  All arrays are device memory,
- * 16-byte aligned (h, B, A_sh, W, u).  Inputs are trusted to be finite and
- * perm to be a permutation of [0, n); ids outside [0, n) give logit 0. */
+/* Runs the three stages in stream order; needs no workspace.  All arrays are
+ * device memory, 16-byte aligned (h, B, A_sh, W, u).  Inputs are trusted to
+ * be finite and perm to be a permutation of [0, n); ids outside [0, n) give
+ * logit 0. */
 sv_status sv_draft_head(const sv_head_args* a, void* stream);
 
 /* Workspace bytes needed by sv_tree_attn (attn != NULL), sv_spec_accept
