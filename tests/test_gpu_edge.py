@@ -124,3 +124,20 @@ def test_root_only_trees_through_verification():
     res = dev.accept_results()
     check_accept(res, ref["accept"], "root only")
     assert res["out_count"].tolist() == [1, 1, 1]        # the bonus token alone
+
+
+def test_no_prefix_at_all():
+    """Every prefix empty (L_max = 0, no cache tensors): attention over the tree
+    only, and the walk, against the oracle."""
+    need_gpu()
+    spec = dict(cfg_id=953, B=3, Hq=8, Hkv=2, D=128, dtype="bf16", logit_dtype="bf16", prefix_len=[0, 0, 0],
+                tree=("dynamic", 1, 4, 1, 5, 1, 20), V=1500, tau=[0.0, 0.8, 1.0], sigma=1.0, draft_std=2.0,
+                sibling_mode="wor", L_max=0)
+    inst = make_instance(spec, 0)
+    assert inst.L_max == 0
+    say("edge: L_max = 0")
+    dev = sv_problem(inst)
+    dev.verify_step()
+    ref = oracle.verify_step(inst)
+    check_attention(dev.attn_result(), ref["attn"], "bf16", label="no prefix")
+    check_accept(dev.accept_results(), ref["accept"], "no prefix")
