@@ -9,10 +9,10 @@
 //                  chunk): reads the chunk of the drafter's probability row
 //                  once into registers and checks the range.  In each wave
 //                  the k-th largest of the lanes' maxima bounds the chunk's
-//                  k-th largest key from below (those k maxima are k keys at
-//                  least that large); the largest of the waves' bounds is
-//                  used, only keys at or above it are gathered in LDS and
-//                  ranked exactly (when very many keys tie at that bound, k
+//                  k-th largest value from below (those k maxima are k tokens
+//                  at least that large); the largest of the waves' bounds is
+//                  used, only tokens at or above it are gathered in LDS as
+//                  exact keys and ranked (when very many tie at that bound, k
 //                  rounds of a block maximum instead).  This is the HBM-bound
 //                  part.
 //   k_expand       one workgroup per sequence: merges the chunks' keys of each
@@ -169,52 +169,59 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
       v[i] = e < hi ? row[e] : 0.0f;
     }
   }
-  bool bad = false;
-  uint64_t mx = 0;
+  // range check and this thread's largest value, on the floats (3 operations
+  // per element); NaN fails v == v
+  float mx = -1.0f, mn = 2.0f;
+  bool nan = false;
 #pragma unroll
   for (int i = 0; i < kEPT; ++i) {
-    const int e = index(i);
-    if (e < hi) {
-      bad |= !(v[i] >= 0.0f && v[i] <= 1.0f);
-      const uint64_t key = prob_key(v[i], e);
-      mx = key > mx ? key : mx;
+    if (index(i) < hi) {
+      mx = fmaxf(mx, v[i]);
+      mn = fminf(mn, v[i]);
+      nan |= !(v[i] == v[i]);
     }
   }
-  __shared__ uint64_t keys_s[kTopkThreads];
+  const bool bad = nan || mn < 0.0f || mx > 1.0f;
+  __shared__ float maxs_s[kTopkThreads];
   __shared__ uint64_t cand_s[kCandCap];
   __shared__ uint64_t wmax[kTopkThreads / 64];
-  __shared__ uint64_t t0_s[kTopkThreads / 64];
+  __shared__ float t0_s[kTopkThreads / 64];
   __shared__ int ncand_s, bad_s;
   uint64_t* out = p.cand + (((size_t)b * p.k + j) * p.nsplit + c) * p.k;
   if (tid == 0) { ncand_s = 0; bad_s = 0; }
-  if (tid < kTopkThreads / 64) t0_s[tid] = 0;
+  if (tid < kTopkThreads / 64) t0_s[tid] = -1.0f;
   if (tid < p.k) out[tid] = 0;
-  keys_s[tid] = mx;
+  maxs_s[tid] = mx;                      // -1 (below every probability) for a thread without tokens
   __syncthreads();
   if (bad) bad_s = 1;
-  // per wave, the k-th largest of its lanes' maxima (0 when fewer than k lanes
-  // hold a token): nonzero maxima are distinct keys, so one lane has rank k - 1
+  // per wave, the k-th largest of its lanes' maxima: the value v with fewer
+  // than k maxima above it and at least k at or above it (-1 when fewer than
+  // k lanes hold a token).  k lanes' maxima are k tokens at least that large,
+  // so it bounds the chunk's k-th largest value from below.
   {
-    const uint64_t* ws = keys_s + (tid & ~63);
-    int r = 0;
+    const float* ws = maxs_s + (tid & ~63);
+    int gt = 0, ge = 0;
 #pragma unroll 8
-    for (int e = 0; e < 64; ++e) r += ws[e] > mx;
-    if (mx != 0 && r == p.k - 1) t0_s[tid >> 6] = mx;
+    for (int e = 0; e < 64; ++e) {
+      gt += ws[e] > mx;
+      ge += ws[e] >= mx;
+    }
+    if (mx >= 0.0f && gt <= p.k - 1 && p.k - 1 < ge) t0_s[tid >> 6] = mx;
   }
   __syncthreads();
-  uint64_t t0 = 0;
+  float t0 = -1.0f;
 #pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) t0 = t0_s[w] > t0 ? t0_s[w] : t0;
+  for (int w = 0; w < kTopkThreads / 64; ++w) t0 = fmaxf(t0, t0_s[w]);
+  // the candidates: every token at or above the bound, as exact keys
   int mine = 0;
 #pragma unroll
-  for (int i = 0; i < kEPT; ++i) mine += index(i) < hi && prob_key(v[i], index(i)) >= t0;
+  for (int i = 0; i < kEPT; ++i) mine += index(i) < hi && v[i] >= t0;
   int at = mine ? atomicAdd(&ncand_s, mine) : 0;
 #pragma unroll
   for (int i = 0; i < kEPT; ++i) {
     const int e = index(i);
-    const uint64_t key = prob_key(v[i], e);
-    if (e < hi && key >= t0) {
-      if (at < kCandCap) cand_s[at] = key;
+    if (e < hi && v[i] >= t0) {
+      if (at < kCandCap) cand_s[at] = prob_key(v[i], e);
       ++at;
     }
   }
