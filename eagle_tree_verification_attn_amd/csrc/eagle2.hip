@@ -37,7 +37,7 @@ constexpr int kCandCap = 1024;                       // gathered candidates per 
 constexpr int kE2MaxK = 16;
 constexpr int kE2MaxSplit = 64;                      // chunks per row: V <= 64 * 8192
 constexpr int kE2StageKeys = kE2MaxSplit * kE2MaxK;  // 1024 keys staged in LDS at a time
-constexpr int kE2Threads = 256;
+constexpr int kE2Threads = 1024;
 constexpr int kFinishThreads = 1024;
 
 struct E2Params {
@@ -371,7 +371,8 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
                                                            int32_t* num_nodes, int32_t* q_row_out,
                                                            int32_t* status_out) {
   constexpr int kMaxNodes = 2048;
-  __shared__ float val_s[kMaxNodes];
+  __shared__ uint64_t nkey_s[kMaxNodes];   // (value, shallower, earlier): larger ranks first
+  __shared__ int rnk_s[kMaxNodes];
   __shared__ int dep_s[kMaxNodes];
   __shared__ int pos_s[kMaxNodes];      // flattened position, -1 if not kept
   __shared__ int par_s[kMaxNodes];
@@ -400,25 +401,41 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
     return;
   }
   for (int i = tid; i < N; i += kFinishThreads) {
-    val_s[i] = p.value[nb + i];
-    dep_s[i] = p.depthv[nb + i];
+    // values are products of probabilities: non-negative, so their bits order
+    // like the values once -0 is made +0; depth and id (< 2048) go below
+    const uint32_t vb = __float_as_uint(p.value[nb + i] + 0.0f);
+    const int dep = p.depthv[nb + i];
+    nkey_s[i] = ((uint64_t)vb << 32) | ((uint32_t)(0xFFFF - dep) << 16) | (uint32_t)(0xFFFF - i);
+    rnk_s[i] = 0;
+    dep_s[i] = dep;
     par_s[i] = p.parent[nb + i];
     rank_s[i] = p.rank[nb + i];
     pos_s[i] = -1;
   }
   __syncthreads();
-  // keep the m best draft nodes: value descending, depth ascending, id ascending
-  for (int i = 1 + tid; i < N; i += kFinishThreads) {
-    const float v = val_s[i];
-    const int d = dep_s[i];
-    int r = 0;
+  // keep the m best draft nodes (value descending, depth ascending, id
+  // ascending): each node's rank counted by several threads over parts of
+  // the nodes, the parts added in LDS
+  {
+    const int M = N - 1;
+    const int parts = M > 0 ? max(1, min(16, kFinishThreads / M)) : 1;
+    const int span = (M + parts - 1) / parts;
+    for (int x = tid; x < M * parts; x += kFinishThreads) {
+      const int i = 1 + x / parts;
+      const int e0 = 1 + (x % parts) * span;
+      const int e1 = min(N, e0 + span);
+      const uint64_t key = nkey_s[i];
+      int r = 0;
 #pragma unroll 8
-    for (int e = 1; e < N; ++e) {
-      const float ve = val_s[e];
-      r += (ve > v) || (ve == v && (dep_s[e] < d || (dep_s[e] == d && e < i)));
+      for (int e = e0; e < e1; ++e) r += nkey_s[e] > key;
+      if (r) atomicAdd(&rnk_s[i], r);
     }
-    pos_s[i] = r < p.m ? 0 : -1;      // 0 marks kept; the position comes below
-    if (r < p.m) kept_s[atomicAdd(&nkept_s, 1)] = i;
+  }
+  __syncthreads();
+  for (int i = 1 + tid; i < N; i += kFinishThreads) {
+    const bool keep = rnk_s[i] < p.m;
+    pos_s[i] = keep ? 0 : -1;         // 0 marks kept; the position comes below
+    if (keep) kept_s[atomicAdd(&nkept_s, 1)] = i;
   }
   if (tid == 0) pos_s[0] = 0;
   __syncthreads();
