@@ -149,39 +149,40 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
   const bool vec = (p.V & 3) == 0;
   // element i of this thread: 16-byte runs when rows are 16-byte aligned
   auto index = [&](int i) { return vec ? lo + 4 * (tid + kTopkThreads * (i >> 2)) + (i & 3) : lo + tid + kTopkThreads * i; };
+  // every load is issued before any is used: addresses past the chunk's end
+  // are clamped to its start, and in(i) below leaves those values out
   float v[kEPT];
-  if (vec) {
+  if (vec) {   // hi is then a multiple of 4 too
 #pragma unroll
     for (int i4 = 0; i4 < kEPT / 4; ++i4) {
       const int e = lo + 4 * (tid + kTopkThreads * i4);
-      if (e + 3 < hi) {
-        const float4 x = *reinterpret_cast<const float4*>(row + e);
-        v[4 * i4] = x.x; v[4 * i4 + 1] = x.y; v[4 * i4 + 2] = x.z; v[4 * i4 + 3] = x.w;
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[4 * i4 + u] = e + u < hi ? row[e + u] : 0.0f;
-      }
+      const float4 x = *reinterpret_cast<const float4*>(row + (e < hi ? e : lo));
+      v[4 * i4] = x.x; v[4 * i4 + 1] = x.y; v[4 * i4 + 2] = x.z; v[4 * i4 + 3] = x.w;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kEPT; ++i) {
       const int e = lo + tid + kTopkThreads * i;
-      v[i] = e < hi ? row[e] : 0.0f;
+      v[i] = row[e < hi ? e : lo];
     }
   }
-  // range check and this thread's largest value, on the floats (3 operations
-  // per element); NaN fails v == v
-  float mx = -1.0f, mn = 2.0f;
-  bool nan = false;
+  // this thread's elements of the chunk are its first nv (all kEPT in a full
+  // chunk, fewer in the last one): in(i) is one compare
+  const int len = hi - lo;
+  const int nv = vec ? 4 * min(kEPT / 4, max(0, (len / 4 - tid + kTopkThreads - 1) / kTopkThreads))
+                     : min(kEPT, max(0, (len - tid + kTopkThreads - 1) / kTopkThreads));
+  auto in = [&](int i) { return i < nv; };
+  // range check and this thread's largest value, without branches: a NaN or
+  // negative value fails v >= 0, a value above 1 shows in the maximum
+  float mx = -1.0f;
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < kEPT; ++i) {
-    if (index(i) < hi) {
-      mx = fmaxf(mx, v[i]);
-      mn = fminf(mn, v[i]);
-      nan |= !(v[i] == v[i]);
-    }
+    const bool ok = in(i);
+    mx = fmaxf(mx, ok ? v[i] : -1.0f);
+    bad |= ok && !(v[i] >= 0.0f);
   }
-  const bool bad = nan || mn < 0.0f || mx > 1.0f;
+  bad |= mx > 1.0f;
   __shared__ float maxs_s[kTopkThreads];
   __shared__ uint64_t cand_s[kCandCap];
   __shared__ uint64_t wmax[kTopkThreads / 64];
@@ -215,13 +216,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
   // the candidates: every token at or above the bound, as exact keys
   int mine = 0;
 #pragma unroll
-  for (int i = 0; i < kEPT; ++i) mine += index(i) < hi && v[i] >= t0;
+  for (int i = 0; i < kEPT; ++i) mine += in(i) && v[i] >= t0;
   int at = mine ? atomicAdd(&ncand_s, mine) : 0;
 #pragma unroll
   for (int i = 0; i < kEPT; ++i) {
-    const int e = index(i);
-    if (e < hi && v[i] >= t0) {
-      if (at < kCandCap) cand_s[at] = prob_key(v[i], e);
+    if (in(i) && v[i] >= t0) {
+      if (at < kCandCap) cand_s[at] = prob_key(v[i], index(i));
       ++at;
     }
   }
@@ -243,9 +243,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
       uint64_t m = 0;
 #pragma unroll
       for (int i = 0; i < kEPT; ++i) {
-        const int e = index(i);
-        const uint64_t key = prob_key(v[i], e);
-        if (e < hi && key < prev && key > m) m = key;
+        const uint64_t key = prob_key(v[i], index(i));
+        if (in(i) && key < prev && key > m) m = key;
       }
       const uint64_t w = wave_max_u64(m);
       if ((tid & 63) == 0) wmax[tid >> 6] = w;
