@@ -22,6 +22,9 @@
 //   k_finish       one workgroup per sequence: ranks every draft node, keeps
 //                  the m best and assigns flattened positions depth by depth.
 //
+// The per-sequence kernels are latency-bound: each issues all of its
+// independent loads at once (one HBM round trip) and then works in LDS.
+//
 // A (probability, token) pair is one 64-bit key: the probability's bits (it is
 // in [0, 1], so its bit pattern orders like its value once -0 is made +0) above
 // the complement of the token.  The larger key is the higher probability, then
@@ -39,11 +42,13 @@ constexpr int kE2MaxSplit = 64;                      // chunks per row: V <= 64 
 constexpr int kE2StageKeys = kE2MaxSplit * kE2MaxK;  // 1024 keys staged in LDS at a time
 constexpr int kE2Threads = 1024;
 constexpr int kFinishThreads = 1024;
+static_assert(kE2StageKeys <= kE2Threads, "expand loads the first group of keys one per thread");
+static_assert(kE2MaxK * kE2MaxSplit <= kE2Threads, "expand loads the range flags one per thread");
 
 struct E2Params {
   int B, V, k, depth, m, nsplit, chunk, nmax;
   int32_t* seq;        // [B][8]: n_nodes, layer_begin, nfront, status
-  int32_t* front;      // [B][16]
+  int4* front;         // [B][16] frontier records: node id, value bits, depth, token
   int32_t* parent;     // [B][nmax]
   int32_t* token;      // [B][nmax]
   int32_t* depthv;     // [B][nmax]
@@ -66,7 +71,7 @@ E2Layout eagle2_layout(const sv_eagle2_cfg* c) {
   const size_t B = (size_t)c->B, N = (size_t)L.nmax, k = (size_t)c->k;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, kWsAlign); return at; };
   L.off_seq = take(B * 8 * 4);
-  L.off_front = take(B * 16 * 4);
+  L.off_front = take(B * 16 * 16);
   L.off_parent = take(B * N * 4);
   L.off_token = take(B * N * 4);
   L.off_depth = take(B * N * 4);
@@ -85,7 +90,7 @@ static E2Params make_params(const sv_eagle2_cfg* c, const E2Layout& L, void* sta
   p.B = c->B; p.V = c->V; p.k = c->k; p.depth = c->depth; p.m = c->m;
   p.nsplit = L.nsplit; p.chunk = L.chunk; p.nmax = L.nmax;
   p.seq = reinterpret_cast<int32_t*>(base + L.off_seq);
-  p.front = reinterpret_cast<int32_t*>(base + L.off_front);
+  p.front = reinterpret_cast<int4*>(base + L.off_front);
   p.parent = reinterpret_cast<int32_t*>(base + L.off_parent);
   p.token = reinterpret_cast<int32_t*>(base + L.off_token);
   p.depthv = reinterpret_cast<int32_t*>(base + L.off_depth);
@@ -124,10 +129,11 @@ __global__ void k_e2_begin(E2Params p, const int32_t* root_tokens) {
   s[kSeqLayer] = 0;
   s[kSeqFront] = 1;
   s[kSeqStatus] = SV_TREE_OK;
-  for (int j = 0; j < 16; ++j) p.front[(size_t)b * 16 + j] = j == 0 ? 0 : -1;
+  const int root = root_tokens[b];
+  p.front[(size_t)b * 16] = make_int4(0, (int)__float_as_uint(1.0f), 0, root);
   const size_t n0 = (size_t)b * p.nmax;
   p.parent[n0] = -1;
-  p.token[n0] = root_tokens[b];
+  p.token[n0] = root;
   p.depthv[n0] = 0;
   p.rank[n0] = 0;
   p.qrow[n0] = -1;
@@ -135,14 +141,17 @@ __global__ void k_e2_begin(E2Params p, const int32_t* root_tokens) {
 }
 
 // ---------------------------------------------------------------- row top-k
-// grid: B * k * nsplit workgroups; workgroup (b, j, c) reads chunk c of row j.
-__global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const float* q) {
+// grid: B * jrows * nsplit workgroups; workgroup (b, j, c) reads chunk c of
+// row j.  jrows is 1 at the first step (the root) and k after it, when every
+// sequence still building has a full frontier; so the row loads go out before
+// the sequence's state is read, and a workgroup of a finished or failed
+// sequence only discards them.
+__global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const float* q, int jrows) {
   const int c = blockIdx.x % p.nsplit;
-  const int j = (blockIdx.x / p.nsplit) % p.k;
-  const int b = blockIdx.x / (p.nsplit * p.k);
+  const int j = (blockIdx.x / p.nsplit) % jrows;
+  const int b = blockIdx.x / (p.nsplit * jrows);
   const int tid = threadIdx.x;
   const int32_t* s = p.seq + (size_t)b * 8;
-  if (s[kSeqStatus] != SV_TREE_OK || j >= s[kSeqFront]) return;
   const int lo = c * kE2Chunk;
   const int hi = min(p.V, lo + kE2Chunk);
   const float* row = q + ((size_t)b * p.k + j) * p.V;
@@ -183,6 +192,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
     bad |= ok && !(v[i] >= 0.0f);
   }
   bad |= mx > 1.0f;
+  if (s[kSeqStatus] != SV_TREE_OK || j >= s[kSeqFront]) return;
   __shared__ float maxs_s[kTopkThreads];
   __shared__ uint64_t cand_s[kCandCap];
   __shared__ uint64_t wmax[kTopkThreads / 64];
@@ -262,6 +272,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
 }
 
 // ---------------------------------------------------------------- expand
+// Every load that does not depend on another goes out first, in one round
+// trip: the sequence's state, its frontier records, the chunks' range flags of
+// all k rows and the first group of chunk keys (all inside the state whatever
+// the frontier's size; only the frontier's rows are used).
 __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int32_t* frontier_out,
                                                        int32_t* frontier_tokens) {
   const int b = blockIdx.x;
@@ -269,22 +283,26 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
   int32_t* s = p.seq + (size_t)b * 8;
   const size_t nb = (size_t)b * p.nmax;
   const int k = p.k;
-  __shared__ uint64_t best_s[kE2MaxK][kE2MaxK];   // per frontier row, its k best keys
-  __shared__ uint64_t row_s[kE2StageKeys];            // chunk candidates of a group of rows
+  const int C = p.nsplit * k;                         // chunk keys per frontier row (<= 1024)
+  const int rows = kE2StageKeys / C;                  // rows staged in LDS at a time (>= 1)
+  const uint64_t* cb = p.cand + (size_t)b * k * C;
+  __shared__ uint64_t best_s[kE2MaxK][kE2MaxK];       // per frontier row, its k best keys
+  __shared__ uint64_t row_s[kE2StageKeys];            // chunk keys of a group of rows
   __shared__ float fval_s[kE2MaxK];
   __shared__ int fnode_s[kE2MaxK], fdep_s[kE2MaxK];
-  __shared__ float val_s[kE2MaxK * kE2MaxK];     // the new layer's values
+  __shared__ float val_s[kE2MaxK * kE2MaxK];          // the new layer's values
   __shared__ int bad_s;
   const int status = s[kSeqStatus];
   const int F = s[kSeqFront];
   const int n0 = s[kSeqN];
+  const int4 rec = tid < k ? p.front[(size_t)b * 16 + tid] : make_int4(-1, 0, 0, -1);
+  const int flag = tid < k * p.nsplit ? p.cand_bad[(size_t)b * k * p.nsplit + tid] : 0;   // k * nsplit <= 1024
+  const int g0 = min(rows, k) * C;                    // <= kE2StageKeys = kE2Threads
+  const uint64_t key0 = tid < g0 ? cb[tid] : 0;
   if (tid == 0) bad_s = 0;
   __syncthreads();
   bool ok = status == SV_TREE_OK;
-  if (ok) {
-    for (int i = tid; i < F * p.nsplit; i += kE2Threads)
-      if (p.cand_bad[((size_t)b * k + i / p.nsplit) * p.nsplit + i % p.nsplit]) bad_s = 1;
-  }
+  if (ok && flag && tid < F * p.nsplit) bad_s = 1;   // a chunk of a frontier row failed the range check
   __syncthreads();
   if (ok && bad_s) {
     ok = false;
@@ -296,20 +314,19 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
     if (tid == 0) s[kSeqStatus] = SV_TREE_E_COUNT;
   }
   if (ok) {
-    // merge: candidate e of row j ranks by the number of row-j candidates
-    // above it; rows are staged in LDS a group at a time
-    const int C = p.nsplit * k;
-    const int rows = kE2StageKeys / C;                 // >= 1 (C <= 1024)
     if (tid < F) {
-      const int node = p.front[(size_t)b * 16 + tid];
-      fnode_s[tid] = node;
-      fval_s[tid] = p.value[nb + node];
-      fdep_s[tid] = p.depthv[nb + node];
+      fnode_s[tid] = rec.x;
+      fval_s[tid] = __int_as_float(rec.y);
+      fdep_s[tid] = rec.z;
     }
+    // merge: key e of row j ranks by the number of row-j keys above it
     for (int j0 = 0; j0 < F; j0 += rows) {
       const int nr = min(rows, F - j0);
-      const uint64_t* cj = p.cand + (size_t)(b * k + j0) * C;
-      for (int i = tid; i < nr * C; i += kE2Threads) row_s[i] = cj[i];
+      if (j0 == 0) {
+        if (tid < nr * C) row_s[tid] = key0;
+      } else {
+        for (int i = tid; i < nr * C; i += kE2Threads) row_s[i] = cb[(size_t)j0 * C + i];
+      }
       __syncthreads();
       for (int i = tid; i < nr * C; i += kE2Threads) {
         const int jj = i / C;
@@ -323,13 +340,13 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
       __syncthreads();
     }
     // children of frontier entry j: ids n0 + j k + r
-    for (int i = tid; i < F * k; i += kE2Threads) {
+    const int Lc = F * k;
+    for (int i = tid; i < Lc; i += kE2Threads) {
       const int j = i / k, r = i % k;
-      const int par = fnode_s[j];
       const uint64_t key = best_s[j][r];
       const float v = __fmul_rn(fval_s[j], key_prob(key));
       const size_t id = nb + n0 + i;
-      p.parent[id] = par;
+      p.parent[id] = fnode_s[j];
       p.token[id] = key_token(key);
       p.depthv[id] = fdep_s[j] + 1;
       p.rank[id] = r;
@@ -337,31 +354,31 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
       p.value[id] = v;
       val_s[i] = v;
     }
-    for (int j = tid; j < F; j += kE2Threads) p.qrow[nb + fnode_s[j]] = step * k + j;
+    if (tid < F) p.qrow[nb + fnode_s[tid]] = step * k + tid;
     __syncthreads();
-    // next frontier: the k best of the new layer (value descending, then id)
-    const int Lc = F * k;
-    if (tid < 16) p.front[(size_t)b * 16 + tid] = -1;
-    __syncthreads();
+    // next frontier: the k best of the new layer (value descending, then id);
+    // Lc >= k, so all k entries are filled
     for (int i = tid; i < Lc; i += kE2Threads) {
       const float v = val_s[i];
       int r = 0;
 #pragma unroll 8
       for (int e = 0; e < Lc; ++e) r += (val_s[e] > v) || (val_s[e] == v && e < i);
-      if (r < k) p.front[(size_t)b * 16 + r] = n0 + i;
+      if (r < k) {
+        const int j = i / k;
+        const int tok = key_token(best_s[j][i % k]);
+        p.front[(size_t)b * 16 + r] = make_int4(n0 + i, (int)__float_as_uint(v), fdep_s[j] + 1, tok);
+        if (frontier_out) frontier_out[(size_t)b * k + r] = n0 + i;
+        if (frontier_tokens) frontier_tokens[(size_t)b * k + r] = tok;
+      }
     }
-    __syncthreads();
     if (tid == 0) {
       s[kSeqLayer] = n0;
       s[kSeqN] = n0 + Lc;
-      s[kSeqFront] = Lc < k ? Lc : k;
+      s[kSeqFront] = k;
     }
-  }
-  __syncthreads();
-  if (tid < k) {
-    const int id = ok ? p.front[(size_t)b * 16 + tid] : -1;
-    if (frontier_out) frontier_out[(size_t)b * k + tid] = id;
-    if (frontier_tokens) frontier_tokens[(size_t)b * k + tid] = id >= 0 ? p.token[nb + id] : -1;
+  } else if (tid < k) {
+    if (frontier_out) frontier_out[(size_t)b * k + tid] = -1;
+    if (frontier_tokens) frontier_tokens[(size_t)b * k + tid] = -1;
   }
 }
 
@@ -384,8 +401,24 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
   const int32_t* s = p.seq + (size_t)b * 8;
   const size_t nb = (size_t)b * p.nmax;
   const int T = p.m + 1;
+  // one round trip: the state and every node slot this thread will handle
+  // (slots at or past the node count hold nothing and are not used)
+  constexpr int kSlots = kMaxNodes / kFinishThreads;
   int status = s[kSeqStatus];
   const int N = s[kSeqN];
+  float valr[kSlots];
+  int depr[kSlots], parr[kSlots], rankr[kSlots], tokr[kSlots], qrr[kSlots];
+#pragma unroll
+  for (int u = 0; u < kSlots; ++u) {
+    const int i = tid + u * kFinishThreads;
+    const bool in = i < p.nmax;
+    valr[u] = in ? p.value[nb + i] : 0.0f;
+    depr[u] = in ? p.depthv[nb + i] : 0;
+    parr[u] = in ? p.parent[nb + i] : -1;
+    rankr[u] = in ? p.rank[nb + i] : 0;
+    tokr[u] = in ? p.token[nb + i] : -1;
+    qrr[u] = in ? p.qrow[nb + i] : -1;
+  }
   if (status == SV_TREE_OK && (N - 1 < p.m || N > p.nmax)) status = SV_TREE_E_COUNT;   // too few steps ran
   if (tid == 0) status_out[b] = status;
   const bool ok = status == SV_TREE_OK;
@@ -399,16 +432,18 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
     if (tid == 0) num_nodes[b] = 0;
     return;
   }
-  for (int i = tid; i < N; i += kFinishThreads) {
+#pragma unroll
+  for (int u = 0; u < kSlots; ++u) {
+    const int i = tid + u * kFinishThreads;
+    if (i >= N) continue;
     // values are products of probabilities: non-negative, so their bits order
     // like the values once -0 is made +0; depth and id (< 2048) go below
-    const uint32_t vb = __float_as_uint(p.value[nb + i] + 0.0f);
-    const int dep = p.depthv[nb + i];
-    nkey_s[i] = ((uint64_t)vb << 32) | ((uint32_t)(0xFFFF - dep) << 16) | (uint32_t)(0xFFFF - i);
+    const uint32_t vb = __float_as_uint(valr[u] + 0.0f);
+    nkey_s[i] = ((uint64_t)vb << 32) | ((uint32_t)(0xFFFF - depr[u]) << 16) | (uint32_t)(0xFFFF - i);
     rnk_s[i] = 0;
-    dep_s[i] = dep;
-    par_s[i] = p.parent[nb + i];
-    rank_s[i] = p.rank[nb + i];
+    dep_s[i] = depr[u];
+    par_s[i] = parr[u];
+    rank_s[i] = rankr[u];
     pos_s[i] = -1;
   }
   __syncthreads();
@@ -462,12 +497,15 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
     base += cnt_s;
     __syncthreads();
   }
-  for (int i = tid; i < N; i += kFinishThreads) {
+#pragma unroll
+  for (int u = 0; u < kSlots; ++u) {
+    const int i = tid + u * kFinishThreads;
+    if (i >= N) continue;
     const int ps = pos_s[i];
     if (ps < 0 || ps >= T) continue;
-    parent_out[(size_t)b * T + ps] = i == 0 ? -1 : pos_s[par_s[i]];
-    tokens_out[(size_t)b * T + ps] = p.token[nb + i];
-    q_row_out[(size_t)b * T + ps] = p.qrow[nb + i];
+    parent_out[(size_t)b * T + ps] = i == 0 ? -1 : pos_s[parr[u]];
+    tokens_out[(size_t)b * T + ps] = tokr[u];
+    q_row_out[(size_t)b * T + ps] = qrr[u];
   }
   if (tid == 0) num_nodes[b] = T;
 }
@@ -488,7 +526,8 @@ sv_status launch_eagle2_expand(const sv_eagle2_cfg* c, void* state, int step, co
   const E2Layout L = eagle2_layout(c);
   const E2Params p = make_params(c, L, state);
   if (c->B == 0) return SV_OK;
-  hipLaunchKernelGGL(k_row_topk, dim3(c->B * c->k * L.nsplit), dim3(kTopkThreads), 0, s, p, q);
+  const int jrows = step == 0 ? 1 : c->k;
+  hipLaunchKernelGGL(k_row_topk, dim3(c->B * jrows * L.nsplit), dim3(kTopkThreads), 0, s, p, q, jrows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) { set_error("eagle2 top-k launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
   hipLaunchKernelGGL(k_expand, dim3(c->B), dim3(kE2Threads), 0, s, p, step, frontier, frontier_tokens);

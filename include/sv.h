@@ -267,8 +267,10 @@ sv_status sv_eagle2_begin(const sv_eagle2_cfg* c, void* state, size_t state_byte
                           const int32_t* root_tokens, void* stream);
 
 /* One expansion step.  q (device, float32 [B][k][V], 16-byte aligned): row j
- * of sequence b is the drafter's probability row for frontier entry j (only
- * row 0, the root's, at step 0; rows beyond the frontier are not read).
+ * of sequence b is the drafter's probability row for frontier entry j.  Step
+ * 0 reads row 0 (the root's) only; later steps read all k rows of every
+ * sequence (the frontier is full then), and a sequence that has failed
+ * ignores what it read.
  * Every row that is read is checked: a value outside [0, 1] or NaN sets the
  * sequence's status to SV_TREE_E_PROB and its later steps do nothing.
  * frontier (device int32 [B][k], may be NULL): the node ids of the next
