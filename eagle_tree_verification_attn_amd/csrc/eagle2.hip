@@ -193,33 +193,35 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
   }
   bad |= mx > 1.0f;
   if (s[kSeqStatus] != SV_TREE_OK || j >= s[kSeqFront]) return;
-  __shared__ float maxs_s[kTopkThreads];
   __shared__ uint64_t cand_s[kCandCap];
   __shared__ uint64_t wmax[kTopkThreads / 64];
   __shared__ float t0_s[kTopkThreads / 64];
   __shared__ int ncand_s, bad_s;
   uint64_t* out = p.cand + (((size_t)b * p.k + j) * p.nsplit + c) * p.k;
   if (tid == 0) { ncand_s = 0; bad_s = 0; }
-  if (tid < kTopkThreads / 64) t0_s[tid] = -1.0f;
   if (tid < p.k) out[tid] = 0;
-  maxs_s[tid] = mx;                      // -1 (below every probability) for a thread without tokens
-  __syncthreads();
-  if (bad) bad_s = 1;
-  // per wave, the k-th largest of its lanes' maxima: the value v with fewer
-  // than k maxima above it and at least k at or above it (-1 when fewer than
-  // k lanes hold a token).  k lanes' maxima are k tokens at least that large,
-  // so it bounds the chunk's k-th largest value from below.
+  // per wave, the k-th largest of its lanes' maxima (-1 when fewer than k
+  // lanes hold a token).  k lanes' maxima are k tokens at least that large,
+  // so it bounds the chunk's k-th largest value from below.  On the maxima's
+  // bits (order-preserving for values in [0, 1] once -0 is made +0; -1 is
+  // negative) it is the largest t with at least k lanes at or above t, built
+  // bit by bit from the top: one compare and one ballot count per bit.
   {
-    const float* ws = maxs_s + (tid & ~63);
-    int gt = 0, ge = 0;
-#pragma unroll 8
-    for (int e = 0; e < 64; ++e) {
-      gt += ws[e] > mx;
-      ge += ws[e] >= mx;
+    const int key = __float_as_int(mx + 0.0f);
+    float tw = -1.0f;
+    if (__popcll(__ballot(key >= 0)) >= p.k) {
+      int t = 0;
+#pragma unroll
+      for (int bit = 30; bit >= 0; --bit) {
+        const int cand = t | (1 << bit);
+        if (__popcll(__ballot(key >= cand)) >= p.k) t = cand;
+      }
+      tw = __int_as_float(t);
     }
-    if (mx >= 0.0f && gt <= p.k - 1 && p.k - 1 < ge) t0_s[tid >> 6] = mx;
+    if ((tid & 63) == 0) t0_s[tid >> 6] = tw;
   }
-  __syncthreads();
+  __syncthreads();   // the bounds, and the counters' initial values
+  if (bad) bad_s = 1;
   float t0 = -1.0f;
 #pragma unroll
   for (int w = 0; w < kTopkThreads / 64; ++w) t0 = fmaxf(t0, t0_s[w]);
@@ -237,6 +239,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
   }
   __syncthreads();
   const int C = ncand_s;
+  if (tid == 0) p.cand_bad[((size_t)b * p.k + j) * p.nsplit + c] = bad_s;   // settled at the barrier above
   if (C <= kCandCap) {
     for (int x = tid; x < C; x += kTopkThreads) {
       const uint64_t key = cand_s[x];
@@ -247,14 +250,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
     }
   } else {
     // very many keys tie at the bound: k rounds, each the block's largest key
-    // below the previous round's
+    // below the previous round's.  The chunk is read again for it (from
+    // cache), so the common path above is all that holds the values in
+    // registers.
     uint64_t prev = ~0ull;
     for (int r = 0; r < p.k; ++r) {
       uint64_t m = 0;
-#pragma unroll
-      for (int i = 0; i < kEPT; ++i) {
-        const uint64_t key = prob_key(v[i], index(i));
-        if (in(i) && key < prev && key > m) m = key;
+#pragma unroll 1
+      for (int i = 0; i < nv; ++i) {
+        const int e = index(i);
+        const uint64_t key = prob_key(row[e], e);
+        if (key < prev && key > m) m = key;
       }
       const uint64_t w = wave_max_u64(m);
       if ((tid & 63) == 0) wmax[tid >> 6] = w;
@@ -267,8 +273,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
       prev = best;
     }
   }
-  __syncthreads();
-  if (tid == 0) p.cand_bad[((size_t)b * p.k + j) * p.nsplit + c] = bad_s;
 }
 
 // ---------------------------------------------------------------- expand

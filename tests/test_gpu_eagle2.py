@@ -74,6 +74,33 @@ def test_builder_matches_oracle(case):
     assert (res["frontier_tokens"][res["frontier"] < 0] == -1).all()
 
 
+@pytest.mark.parametrize("V", [20000, 9001])
+def test_builder_heavy_ties(V):
+    """Rows where thousands of tokens tie at the k-th value: more keys sit at
+    the chunk's bound than its candidate list holds, so the chunk's k best
+    come from rounds of a block maximum instead (the path that reads the chunk
+    again).  Sequence 0: uniform rows.  Sequence 1: three large values, every
+    other token equal.  Sequence 2: ordinary rows.  V = 9001 also covers rows
+    that are not 16-byte runs."""
+    need_gpu()
+    B, k, depth, m = 3, 5, 3, 20
+    q = make_draft_rows(B, k, depth, V, seed=V)
+    for s in range(depth):
+        q[s][0] = np.float32(1.0 / V)
+        q[s][1] = np.float32(0.25 / V)
+        for j in range(k):
+            q[s][1, j, [17 + j, V // 2 + 3 * j, V - 1 - j]] = np.float32([0.3, 0.2, 0.1])
+    roots = np.array([1, 2, 3], dtype=np.int32)
+    say(f"eagle2 heavy ties V={V}")
+    ref = eagle2.build(q, roots, k, depth, m)
+    assert (ref["status"] == eagle2.TREE_OK).all()
+    res = _run(B, V, k, depth, m, q, roots)
+    _check(res, ref, label=f"ties V={V}")
+    # uniform rows: the children of every node are the k lowest token ids
+    kids = res["tokens"][0][res["parent"][0] == 0]
+    assert sorted(kids.tolist()) == list(range(k))
+
+
 def test_invalid_rows_mark_only_their_sequence():
     need_gpu()
     B, V, k, depth, m = 6, 800, 3, 3, 10
