@@ -120,6 +120,23 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Largest 64-bit key over each row of 16 lanes, in every lane of the row:
+// DPP lane permutations within the row (pairs, quads, half rows, the row).
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ inline uint64_t row16_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v);  v = o > v ? o : v;    // quad_perm [1, 0, 3, 2]
+  o = dpp_u64<0x4E>(v);  v = o > v ? o : v;    // quad_perm [2, 3, 0, 1]
+  o = dpp_u64<0x141>(v); v = o > v ? o : v;    // row_half_mirror
+  o = dpp_u64<0x140>(v); v = o > v ? o : v;    // row_mirror
+  return v;
+}
+
 // ---------------------------------------------------------------- begin
 __global__ void k_e2_begin(E2Params p, const int32_t* root_tokens) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -323,7 +340,16 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
       fval_s[tid] = __int_as_float(rec.y);
       fdep_s[tid] = rec.z;
     }
-    // merge: key e of row j ranks by the number of row-j keys above it
+    // merge: a chunk's k keys come sorted (largest first, 0-padded), so each
+    // row's k best are a k-way merge of its chunks' lists.  Row jj of a group
+    // belongs to one 16-lane row of a wave; lane l of it holds the heads of
+    // chunks l, l + 16, l + 32 and l + 48.  Each round takes the largest head
+    // of the 16 lanes and advances the list it came from (keys are distinct,
+    // since their tokens are).
+    const int lane = tid & 63;
+    const int jj = (tid >> 6) * 4 + (lane >> 4);       // up to 64 rows per group
+    const int gl = lane & 15;
+    const int nu = (p.nsplit + 15) / 16;                // chunks per lane, <= 4
     for (int j0 = 0; j0 < F; j0 += rows) {
       const int nr = min(rows, F - j0);
       if (j0 == 0) {
@@ -332,14 +358,30 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
         for (int i = tid; i < nr * C; i += kE2Threads) row_s[i] = cb[(size_t)j0 * C + i];
       }
       __syncthreads();
-      for (int i = tid; i < nr * C; i += kE2Threads) {
-        const int jj = i / C;
-        const uint64_t* rs = row_s + jj * C;
-        const uint64_t x = row_s[i];
-        int r = 0;
-#pragma unroll 8
-        for (int e = 0; e < C; ++e) r += rs[e] > x;
-        if (x != 0 && r < k) best_s[j0 + jj][r] = x;
+      const bool live = jj < nr;
+      const uint64_t* rs = row_s + (live ? jj : 0) * C;
+      uint64_t head[4];
+      int pos[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = gl + 16 * u;
+        pos[u] = 0;
+        head[u] = (live && u < nu && c < p.nsplit) ? rs[c * k] : 0;
+      }
+      for (int r = 0; r < k; ++r) {
+        uint64_t mine = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mine = head[u] > mine ? head[u] : mine;
+        const uint64_t best = row16_max_u64(mine);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (best != 0 && head[u] == best) {
+            const int c = gl + 16 * u;
+            ++pos[u];
+            head[u] = pos[u] < k ? rs[c * k + pos[u]] : 0;
+          }
+        }
+        if (live && gl == 0) best_s[j0 + jj][r] = best;
       }
       __syncthreads();
     }
