@@ -11,10 +11,12 @@
 //                  tiles are summed in LDS in a fixed order and rounded to
 //                  bf16 (the operand of the next stage).
 //   k_head_topk    one workgroup per vocabulary tile: scores^T = A_tile u^T on
-//                  MFMA into LDS (never written to HBM), then per position the
-//                  k_tile best rows by wave argmax rounds over 64-bit keys
-//                  (order-preserving score bits above the complement of the
-//                  row), written as token ids through the shuffle.
+//                  MFMA into LDS (never written to HBM), each wave loading its
+//                  two row blocks and the shared u fragments in one batch;
+//                  then per position the k_tile best rows by rounds of a DPP
+//                  wave maximum over 64-bit keys (order-preserving score bits
+//                  above the complement of the row), written as token ids
+//                  through the shuffle (read with the first loads).
 //   k_head_logits  one wave per (position, candidate): the candidate's row of
 //                  W gathered once and dotted with h in float32.
 //
@@ -57,17 +59,6 @@ __device__ inline uint16_t bf16_rne(float x) {
 __device__ inline uint32_t sortable(float x) {
   const uint32_t b = __float_as_uint(x);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ inline uint64_t wave_max64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, off);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
 }
 
 // ---------------------------------------------------------------- stage 1
@@ -113,9 +104,14 @@ __global__ __launch_bounds__(64 * kUWaves) void k_head_u(HeadParams p) {
 
 // ---------------------------------------------------------------- stage 2
 // grid (n_tiles, ceil(N / 16)); 8 waves; wave w scores the tile's 16-row
-// blocks w, w + 8, ...
+// blocks w and w + 8, loading both blocks' A fragments and the u fragments
+// they share in one batch (per 8 k-steps).  The tile's token ids are read
+// with them and staged in LDS, so the selection needs no further global
+// read.
 __global__ __launch_bounds__(64 * kTopkWaves) void k_head_topk(HeadParams p) {
+  constexpr int kRB = kHeadTileMax / 16 / kTopkWaves;   // row blocks per wave
   __shared__ float sc_s[kHeadTileMax][17];      // [row in tile][position], padded
+  __shared__ int perm_s[kHeadTileMax];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
   const int n0 = blockIdx.y * 16;
@@ -125,28 +121,43 @@ __global__ __launch_bounds__(64 * kTopkWaves) void k_head_topk(HeadParams p) {
   const int pos = n0 + (lane & 15);
   const bool pos_ok = pos < p.N;
   const int ksteps = p.r / 32;
+  static_assert(kHeadTileMax <= 64 * kTopkWaves, "one token id per thread");
+  const int prm = tid < rows ? p.perm[lo + tid] : 0;   // to LDS once the loads below are in
   const __bf16* urow = p.u + (size_t)(pos_ok ? pos : 0) * p.r + 8 * kg;
+  const __bf16* arow[kRB];
+  bool row_ok[kRB];
+#pragma unroll
+  for (int q = 0; q < kRB; ++q) {
+    const int row = (wave + kTopkWaves * q) * 16 + (lane & 15);
+    row_ok[q] = row < rows;
+    arow[q] = p.A + (size_t)(lo + (row_ok[q] ? row : 0)) * p.r + 8 * kg;
+  }
   const bf16x8 zero = {};
-  // 16-row blocks of the tile, round robin over the waves
-  for (int rb = wave; rb * 16 < rows; rb += kTopkWaves) {
-    const int row = rb * 16 + (lane & 15);
-    const bool row_ok = row < rows;
-    const __bf16* arow = p.A + (size_t)(lo + (row_ok ? row : 0)) * p.r + 8 * kg;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ksteps; s0 += 8) {
-      bf16x8 a[8], b[8];
+  f32x4 acc[kRB];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bool ok = s0 + s < ksteps;
-        a[s] = ok && row_ok ? load8(arow + 32 * (s0 + s)) : zero;
-        b[s] = ok && pos_ok ? load8(urow + 32 * (s0 + s)) : zero;
-      }
+  for (int q = 0; q < kRB; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < ksteps; s0 += 8) {
+    bf16x8 a[kRB][8], b[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        if (s0 + s < ksteps) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
+    for (int s = 0; s < 8; ++s) {
+      const bool ok = s0 + s < ksteps;
+      b[s] = ok && pos_ok ? load8(urow + 32 * (s0 + s)) : zero;
+#pragma unroll
+      for (int q = 0; q < kRB; ++q) a[q][s] = ok && row_ok[q] ? load8(arow[q] + 32 * (s0 + s)) : zero;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc_s[rb * 16 + 4 * kg + i][lane & 15] = acc[i];
+    for (int s = 0; s < 8; ++s)
+      if (s0 + s < ksteps)
+#pragma unroll
+        for (int q = 0; q < kRB; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][s], b[s], acc[q], 0, 0, 0);
+  }
+  if (tid < rows) perm_s[tid] = prm;
+#pragma unroll
+  for (int q = 0; q < kRB; ++q) {
+    const int rb = wave + kTopkWaves * q;
+    if (rb * 16 < rows)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc_s[rb * 16 + 4 * kg + i][lane & 15] = acc[q][i];
   }
   __syncthreads();
   // per position: the k_tile best rows (score descending, then row ascending)
@@ -167,11 +178,11 @@ __global__ __launch_bounds__(64 * kTopkWaves) void k_head_topk(HeadParams p) {
         uint64_t m = 0;
 #pragma unroll
         for (int j = 0; j < kHeadTileMax / 64; ++j) m = key[j] > m ? key[j] : m;
-        const uint64_t best = wave_max64(m);
+        const uint64_t best = wave_max_u64_dpp(m);
         const int row = (int)~(uint32_t)best;
 #pragma unroll
         for (int j = 0; j < kHeadTileMax / 64; ++j) key[j] = key[j] == best ? 0 : key[j];
-        id = p.perm[lo + row];
+        id = perm_s[row];
       }
       if (lane == 0) ids[c] = id;
     }

@@ -120,23 +120,6 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// Largest 64-bit key over each row of 16 lanes, in every lane of the row:
-// DPP lane permutations within the row (pairs, quads, half rows, the row).
-template <int CTRL>
-__device__ inline uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-__device__ inline uint64_t row16_max_u64(uint64_t v) {
-  uint64_t o;
-  o = dpp_u64<0xB1>(v);  v = o > v ? o : v;    // quad_perm [1, 0, 3, 2]
-  o = dpp_u64<0x4E>(v);  v = o > v ? o : v;    // quad_perm [2, 3, 0, 1]
-  o = dpp_u64<0x141>(v); v = o > v ? o : v;    // row_half_mirror
-  o = dpp_u64<0x140>(v); v = o > v ? o : v;    // row_mirror
-  return v;
-}
-
 // ---------------------------------------------------------------- begin
 __global__ void k_e2_begin(E2Params p, const int32_t* root_tokens) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;

@@ -17,6 +17,38 @@ constexpr size_t kWsAlign = 256;    // workspace sub-buffer alignment
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Largest 64-bit value over each row of 16 lanes, in every lane of the row:
+// DPP lane permutations within the row (pairs, quads, half rows, the row).
+// Every lane of the row must be active.
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ inline uint64_t row16_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v);  v = o > v ? o : v;    // quad_perm [1, 0, 3, 2]
+  o = dpp_u64<0x4E>(v);  v = o > v ? o : v;    // quad_perm [2, 3, 0, 1]
+  o = dpp_u64<0x141>(v); v = o > v ? o : v;    // row_half_mirror
+  o = dpp_u64<0x140>(v); v = o > v ? o : v;    // row_mirror
+  return v;
+}
+// Largest 64-bit value over the wave (uniform): the four row maxima, read
+// from the last lane of each row.  Every lane must be active.
+__device__ inline uint64_t wave_max_u64_dpp(uint64_t v) {
+  v = row16_max_u64(v);
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r + 15);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r + 15);
+    const uint64_t x = ((uint64_t)hi << 32) | lo;
+    m = x > m ? x : m;
+  }
+  return m;
+}
+
 // Thread-local detail string behind sv_last_error().
 void set_error(const char* fmt, ...);
 void clear_error();
