@@ -219,6 +219,28 @@ def time_commit(dev, inst, res, n, stream):
     return ms, float(2 * 2 * rows * inst.Hkv * inst.D * s)     # K and V rows, read and written
 
 
+def stream_rates(stream, n=10):
+    """Measured HBM rates on this GPU for context: a read-only stream (torch
+    row sums over 1 GiB of float32 in rows of 4096: reads 1 GiB, writes 256 KB;
+    the fastest of the torch reductions tried) and a copy (1 GiB in, 1 GiB
+    out), each averaged over n launches between HIP events."""
+    import torch
+    nbytes = 1 << 30
+    x = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    rows = x.view(-1, 4096)
+    for _ in range(2):
+        rows.sum(1)
+        y.copy_(x)
+    read_ms = time_launches(lambda: rows.sum(1), n, stream)
+    copy_ms = time_launches(lambda: y.copy_(x), n, stream)
+    del x, y, rows
+    torch.cuda.empty_cache()
+    return {"read_only_GB_s": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
+            "copy_GB_s": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1),
+            "note": "row sums over 1 GiB float32, rows of 4096 (read-only stream); 1 GiB device copy (read + write)"}
+
+
 def time_eagle2(inst, n, stream):
     """One EAGLE-2 tree build (begin, one expand per step, finish) for the
     batch: k = 8, 6 steps, m = T_max - 1 kept nodes (the batch's tree size),
@@ -396,6 +418,9 @@ def main():
     commit_ms, commit_bytes = time_commit(dev, inst, res, n, stream)
     e2 = time_eagle2(inst, n, stream)
     head = time_draft_head(inst, n, stream)
+    rates = stream_rates(stream)
+    for d in (e2, head):
+        d["frac_of_measured_read"] = round(d["GB_s"] / rates["read_only_GB_s"], 4)
     flops, attn_bytes = algorithmic_work(inst)
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
@@ -445,7 +470,8 @@ def main():
         "draft_head": head,
         "hbm_roofline": {"tree_attn_verify": {"algorithmic_bytes": attn_bytes,
                                               "GB_s": round(attn_gbs, 1),
-                                              "frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
+                                              "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                                              "frac_of_measured_read": round(attn_gbs / rates["read_only_GB_s"], 4)},
                          "tree_spec_accept": {"algorithmic_bytes": acc_bytes,
                                               "GB_s": round(acc_gbs, 1),
                                               "frac": round(acc_gbs / HBM_PEAK_GBS, 4),
@@ -454,7 +480,8 @@ def main():
                                               # read's time at peak, against this walk's time
                                               "every_row_once_bytes": every_row_bytes,
                                               "every_row_once_roofline_ms": round(every_row_ms, 5),
-                                              "walk_ms_vs_that_roofline": round(acc_ms / every_row_ms, 4)}},
+                                              "walk_ms_vs_that_roofline": round(acc_ms / every_row_ms, 4)},
+                         "measured_stream": rates},
         "emitted_tokens_per_seq": round(float(np.mean(res["out_count"])), 3),
         "vocab_passes_per_seq": round(float(np.mean(res["out_passes"])), 3),
     }
