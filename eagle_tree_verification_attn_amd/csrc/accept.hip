@@ -651,6 +651,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
 // ----------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------
+int accept_exchange_words(const AcceptPlan& pl) { return pl.ngroups * 2 * pl.nchunk * kXWords; }
+
 bool plan_accept(const sv_tree* t, const sv_accept_args* a, AcceptPlan* pl) {
   const DeviceInfo& di = device_info();
   *pl = AcceptPlan{};
@@ -675,13 +677,13 @@ bool plan_accept(const sv_tree* t, const sv_accept_args* a, AcceptPlan* pl) {
   pl->ngroups = ngroups;
   size_t off = 0;
   pl->off_xchg = off;
-  off += align_up((size_t)ngroups * 2 * nchunk * kXWords * sizeof(uint64_t), kWsAlign);
+  off += align_up((size_t)accept_exchange_words(*pl) * sizeof(uint64_t), kWsAlign);
   pl->ws_bytes = off;
   return true;
 }
 
 sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_args* a,
-                        const AcceptPlan& pl, void* ws, hipStream_t s) {
+                        const AcceptPlan& pl, void* ws, bool clear_exchange, hipStream_t s) {
   if (t->B == 0) return SV_OK;
   char* wsb = static_cast<char*>(ws);
   WalkParams wp{};
@@ -708,12 +710,16 @@ sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_
   wp.bf16 = a->logit_dtype == SV_BF16;
   wp.sibling_mode = a->sibling_mode;
   // exchange words start at zero on every call (a fill kernel: no memset
-  // node, so the call can be captured in a graph)
-  hipLaunchKernelGGL(k_accept_clear, dim3(1), dim3(256), 0, s, wp.xchg, pl.ngroups * 2 * pl.nchunk * kXWords);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_error("accept clear launch: %s", hipGetErrorString(e));
-    return SV_E_HIP;
+  // node, so the call can be captured in a graph; a verify step's mask kernel
+  // zeroes them instead)
+  hipError_t e = hipSuccess;
+  if (clear_exchange) {
+    hipLaunchKernelGGL(k_accept_clear, dim3(1), dim3(256), 0, s, wp.xchg, accept_exchange_words(pl));
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      set_error("accept clear launch: %s", hipGetErrorString(e));
+      return SV_E_HIP;
+    }
   }
   // 16-byte vector loads: V % 8 == 0 and 16-byte aligned rows of logits and q
   const bool vec = (a->V % 8) == 0 && (reinterpret_cast<uintptr_t>(a->target_logits) % 16) == 0 &&

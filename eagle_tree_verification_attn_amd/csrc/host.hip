@@ -167,7 +167,7 @@ sv_status sv_tree_mask_build(const sv_tree* tree, uint64_t* anc, int32_t* depth,
   sv_status st = check_tree(tree, false);
   if (st) return st;
   if (tree->B > 0 && (!anc || !depth || !tree_status)) { set_error("anc/depth/tree_status is NULL"); return SV_E_NULL; }
-  return launch_mask(tree, anc, depth, tree_status, (hipStream_t)stream);
+  return launch_mask(tree, anc, depth, tree_status, nullptr, 0, (hipStream_t)stream);
 }
 
 sv_status sv_tree_attn(const sv_tree* tree, const uint64_t* anc, const int32_t* tree_status,
@@ -193,7 +193,7 @@ sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_acc
   AcceptPlan pl;
   if (!plan_accept(tree, a, &pl)) { set_error("no accept plan"); return SV_E_UNSUPPORTED; }
   if ((st = check_ws(ws, ws_bytes, pl.ws_bytes))) return st;
-  return launch_accept(tree, tree_status, a, pl, ws, (hipStream_t)stream);
+  return launch_accept(tree, tree_status, a, pl, ws, true, (hipStream_t)stream);
 }
 
 sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
@@ -209,12 +209,17 @@ sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv
   AcceptPlan cp;
   if (!plan_attention(tree, attn, &ap)) { set_error("no attention plan"); return SV_E_UNSUPPORTED; }
   if (!plan_accept(tree, acc, &cp)) { set_error("no accept plan"); return SV_E_UNSUPPORTED; }
-  const size_t need = ap.ws_bytes > cp.ws_bytes ? ap.ws_bytes : cp.ws_bytes;
-  if ((st = check_ws(ws, ws_bytes, need))) return st;
+  // the walk's exchange words follow the attention's partial results, so the
+  // mask kernel can zero them before attention runs
+  const size_t acc_base = align_up(ap.ws_bytes, kWsAlign);
+  cp.off_xchg += acc_base;
+  if ((st = check_ws(ws, ws_bytes, acc_base + cp.ws_bytes))) return st;
   hipStream_t s = (hipStream_t)stream;
-  if ((st = launch_mask(tree, anc, depth, tree_status, s))) return st;
+  uint64_t* xchg = tree->B > 0 ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + cp.off_xchg) : nullptr;
+  if ((st = launch_mask(tree, anc, depth, tree_status, xchg, tree->B > 0 ? accept_exchange_words(cp) : 0, s)))
+    return st;
   if ((st = launch_attention(tree, anc, tree_status, attn, ap, ws, s))) return st;
-  return launch_accept(tree, tree_status, acc, cp, ws, s);
+  return launch_accept(tree, tree_status, acc, cp, ws, false, s);
 }
 
 sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const int32_t* out_nodes,
@@ -332,7 +337,8 @@ size_t sv_workspace_bytes(const sv_tree* tree, const sv_attn_args* attn, const s
     if (acc->V < 1) { set_error("V = %d < 1", acc->V); return 0; }
     AcceptPlan pl;
     if (!plan_accept(tree, acc, &pl)) { set_error("V = %d unsupported", acc->V); return 0; }
-    if (pl.ws_bytes > need) need = pl.ws_bytes;
+    // both: the layout of sv_verify_step, the walk's words after the attention's
+    need = attn ? align_up(need, kWsAlign) + pl.ws_bytes : pl.ws_bytes;
   }
   return need;
 }

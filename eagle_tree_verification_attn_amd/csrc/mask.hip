@@ -8,7 +8,8 @@
 //
 // One workgroup of 256 threads per sequence; thread i owns row i.  The tree is
 // validated first (node count, root, parent[i] < i), so every parent walk
-// strictly decreases and ends at the root.
+// strictly decreases and ends at the root.  In a verify step the kernel also
+// zeroes the walk's exchange words, which saves the walk its own fill kernel.
 #include "sv_internal.h"
 
 namespace sv {
@@ -18,11 +19,13 @@ __global__ __launch_bounds__(256) void k_tree_mask_build(const int32_t* __restri
                                                          int T_max, int W,
                                                          uint64_t* __restrict__ anc,
                                                          int32_t* __restrict__ depth,
-                                                         int32_t* __restrict__ tree_status) {
+                                                         int32_t* __restrict__ tree_status,
+                                                         uint64_t* __restrict__ zero_words, int n_zero) {
   __shared__ int par[kMaxT];
   __shared__ int flags;  // bit 0: root has a parent, bit 1: a parent out of range
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  for (int i = b * 256 + tid; i < n_zero; i += gridDim.x * 256) zero_words[i] = 0ull;
   const int Tb = num_nodes[b];
   const bool count_ok = Tb >= 1 && Tb <= T_max;
   if (tid == 0) flags = 0;
@@ -69,11 +72,11 @@ __global__ __launch_bounds__(256) void k_tree_mask_build(const int32_t* __restri
 }
 
 sv_status launch_mask(const sv_tree* t, uint64_t* anc, int32_t* depth, int32_t* tree_status,
-                      hipStream_t s) {
+                      uint64_t* zero_words, int n_zero, hipStream_t s) {
   if (t->B == 0) return SV_OK;
   const int W = (t->T_max + 63) / 64;
   hipLaunchKernelGGL(k_tree_mask_build, dim3(t->B), dim3(256), 0, s, t->parent, t->num_nodes,
-                     t->T_max, W, anc, depth, tree_status);
+                     t->T_max, W, anc, depth, tree_status, zero_words, n_zero);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("mask build launch: %s", hipGetErrorString(e));

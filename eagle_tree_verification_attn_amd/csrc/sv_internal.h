@@ -85,8 +85,11 @@ struct AcceptPlan {
   size_t ws_bytes;
 };
 bool plan_accept(const sv_tree* t, const sv_accept_args* a, AcceptPlan* p);
+int accept_exchange_words(const AcceptPlan& p);   // uint64 words at off_xchg
+// clear_exchange: zero the exchange words first (a fill kernel); false when
+// the caller's stream already zeroed them (the mask kernel of a verify step)
 sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_args* a,
-                        const AcceptPlan& p, void* ws, hipStream_t s);
+                        const AcceptPlan& p, void* ws, bool clear_exchange, hipStream_t s);
 
 // ---------------------------------------------------------------- commit
 sv_status launch_commit(const sv_tree* t, int32_t* tree_status, const int32_t* out_nodes,
@@ -111,7 +114,9 @@ sv_status launch_eagle2_finish(const sv_eagle2_cfg* c, const void* state, int32_
 sv_status launch_draft_head(const sv_head_args* a, hipStream_t s);
 
 // ---------------------------------------------------------------- mask
+// zero_words / n_zero: words the mask kernel also zeroes (a verify step's
+// exchange words for the walk), or NULL / 0
 sv_status launch_mask(const sv_tree* t, uint64_t* anc, int32_t* depth, int32_t* tree_status,
-                      hipStream_t s);
+                      uint64_t* zero_words, int n_zero, hipStream_t s);
 
 }  // namespace sv

@@ -327,8 +327,10 @@ typedef struct {
 sv_status sv_draft_head(const sv_head_args* a, void* stream);
 
 /* Workspace bytes needed by sv_tree_attn (attn != NULL), sv_spec_accept
- * (acc != NULL) or both (the maximum).  Host only; reads only the scalar
- * fields of the structs.  Returns 0 on invalid sizes (see sv_last_error). */
+ * (acc != NULL) or sv_verify_step (both: the attention's region followed by
+ * the accept's, which is enough for either call alone too).  Host only;
+ * reads only the scalar fields of the structs.  Returns 0 on invalid sizes
+ * (see sv_last_error). */
 size_t sv_workspace_bytes(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc);
 
 /* Static description of a status code (host or tree status). */

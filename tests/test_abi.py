@@ -111,9 +111,12 @@ def test_workspace_sizes_for_the_workloads():
                   dtype=sv.SV_BF16 if c["dtype"] == "bf16" else sv.SV_F32)
         acc = _acc(V=c["V"])
         n_acc = sv.sv_workspace_bytes(t, None, acc)
+        n_attn = sv.sv_workspace_bytes(t, a, None)
         n_both = sv.sv_workspace_bytes(t, a, acc)
         assert n_acc > 0 and n_both >= n_acc
         assert n_both % 256 == 0
+        # the step's layout: the accept's words after the attention's partial results
+        assert n_both == -(-n_attn // 256) * 256 + n_acc
 
 
 # ---------------------------------------------------------------- tree builder (host checks only)
