@@ -184,7 +184,10 @@ sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_acc
 
 /* One verification step: sv_tree_mask_build, then sv_tree_attn, then
  * sv_spec_accept, in stream order, sharing one workspace of at least
- * sv_workspace_bytes(tree, attn, acc) bytes. */
+ * sv_workspace_bytes(tree, attn, acc) bytes: the attention's partial results
+ * first, then the accept's exchange words, which the mask kernel zeroes (so
+ * the step launches three kernels).  Results are those of the three calls
+ * made one after another. */
 sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
                          uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws,
                          size_t ws_bytes, void* stream);
