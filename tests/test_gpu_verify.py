@@ -1,5 +1,7 @@
 """The whole step (sv_verify_step: mask -> attention -> accept on one stream,
 one workspace) against the oracle, and its repeatability."""
+import os
+
 import numpy as np
 import pytest
 
@@ -53,3 +55,24 @@ def test_verify_step_repeatable():
         assert torch.equal(dev.out.view(torch.int16), first[0].view(torch.int16))
         assert torch.equal(dev.out_tokens, first[1]) and torch.equal(dev.out_nodes, first[2])
         assert torch.equal(dev.out_count, first[3])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_verify_step_split_keys(dtype):
+    """Key ranges split four ways: the attention's partial results and the
+    walk's exchange words share the step's workspace (the words after the
+    partials, zeroed by the mask kernel)."""
+    need_gpu()
+    spec = dict(cfg_id=402, B=3, Hq=8, Hkv=2, D=64, dtype=dtype, logit_dtype="bf16" if dtype == "bf16" else "f32",
+                prefix_len=[900, 0, 2500], tree=("widths", [3, 6, 6]), V=7000, tau=("choice", [0.0, 0.9]),
+                sigma=1.0, draft_std=3.0, sibling_mode="wor")
+    inst = make_instance(spec, 2)
+    old = os.environ.get("SV_ATTN_LSPLIT")
+    os.environ["SV_ATTN_LSPLIT"] = "4"
+    try:
+        _step(inst, f"split keys {dtype}")
+    finally:
+        if old is None:
+            os.environ.pop("SV_ATTN_LSPLIT", None)
+        else:
+            os.environ["SV_ATTN_LSPLIT"] = old
