@@ -10,6 +10,9 @@
 //                  dim with 8 k-steps of loads in flight; the waves' partial
 //                  tiles are summed in LDS in a fixed order and rounded to
 //                  bf16 (the operand of the next stage).
+//   k_head_u_small the same for N <= 16 positions (a drafter step) on VALU:
+//                  2 rank rows per workgroup, so r / 2 workgroups share B's
+//                  read instead of r / 16.
 //   k_head_topk    one workgroup per vocabulary tile: scores^T = A_tile u^T on
 //                  MFMA into LDS (never written to HBM), each wave loading its
 //                  two row blocks and the shared u fragments in one batch;
@@ -31,7 +34,10 @@ namespace sv {
 constexpr int kHeadMaxK = 8;      // candidates per tile
 constexpr int kHeadTileMax = 256; // vocabulary rows per tile
 
-constexpr int kUWaves = 16;       // stage-1 waves per workgroup
+constexpr int kUWaves = 16;       // stage-1 waves per workgroup (MFMA kernel)
+constexpr int kUSmallN = 16;      // positions up to which stage 1 runs on VALU
+constexpr int kURows = 2;         // rank rows per workgroup of the VALU kernel
+constexpr int kUThreads = 512;    // threads of the VALU kernel
 constexpr int kTopkWaves = 8;     // stage-2 waves per workgroup
 
 struct HeadParams {
@@ -47,6 +53,7 @@ struct HeadParams {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline bf16x8 load8(const __bf16* p) { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p)); }
 
@@ -99,6 +106,75 @@ __global__ __launch_bounds__(64 * kUWaves) void k_head_u(HeadParams p) {
     uint16_t* u = reinterpret_cast<uint16_t*>(p.u) + (size_t)pos * p.r + r0 + 4 * kg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) u[i] = bf16_rne(t[i]);
+  }
+}
+
+// Few positions (N <= 16): u = B h is a few MFLOP, and the MFMA kernel above
+// has only r / 16 workgroups to spread B's read over.  Here each workgroup
+// takes 2 rank rows for every position, so r / 2 workgroups read B.  Thread t
+// takes the 8-element groups t, t + 512, ... of the hidden dim, two groups per
+// batch of loads, with bf16 pair dots accumulated in float32.  The partial
+// sums are added in a fixed order: a shuffle butterfly within each wave,
+// then the 8 waves in turn; u is rounded to bf16 once.
+__device__ inline float dot8(bf16x8 a, bf16x8 b, float c) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 x = {a[2 * e], a[2 * e + 1]};
+    const bf16x2 y = {b[2 * e], b[2 * e + 1]};
+    c = __builtin_amdgcn_fdot2_f32_bf16(x, y, c, false);
+  }
+  return c;
+}
+
+__global__ __launch_bounds__(kUThreads) void k_head_u_small(HeadParams p) {
+  __shared__ float red_s[kUThreads / 64][kURows * kUSmallN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = blockIdx.x * kURows;
+  const bf16x8 zero = {};
+  float acc[kURows][kUSmallN];
+#pragma unroll
+  for (int rr = 0; rr < kURows; ++rr)
+#pragma unroll
+    for (int n = 0; n < kUSmallN; ++n) acc[rr][n] = 0.f;
+  constexpr int kStep = 8 * kUThreads;                 // hidden-dim elements per group sweep
+  for (int k0 = 8 * tid; k0 < p.d; k0 += 2 * kStep) {
+    bf16x8 b[2][kURows], h[2][kUSmallN];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int k = k0 + g * kStep;
+      const bool ok = k < p.d;
+#pragma unroll
+      for (int rr = 0; rr < kURows; ++rr) b[g][rr] = ok ? load8(p.B + (size_t)(r0 + rr) * p.d + k) : zero;
+#pragma unroll
+      for (int n = 0; n < kUSmallN; ++n) h[g][n] = ok && n < p.N ? load8(p.h + (size_t)n * p.d + k) : zero;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int rr = 0; rr < kURows; ++rr)
+#pragma unroll
+        for (int n = 0; n < kUSmallN; ++n)
+          if (n < p.N) acc[rr][n] = dot8(b[g][rr], h[g][n], acc[rr][n]);
+  }
+#pragma unroll
+  for (int rr = 0; rr < kURows; ++rr)
+#pragma unroll
+    for (int n = 0; n < kUSmallN; ++n) {
+      if (n >= p.N) continue;
+      float v = acc[rr][n];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0) red_s[wave][rr * kUSmallN + n] = v;
+    }
+  __syncthreads();
+  if (tid < kURows * kUSmallN) {
+    const int rr = tid / kUSmallN, n = tid % kUSmallN;
+    if (n < p.N) {
+      float t = red_s[0][tid];
+#pragma unroll
+      for (int w = 1; w < kUThreads / 64; ++w) t += red_s[w][tid];
+      reinterpret_cast<uint16_t*>(p.u)[(size_t)n * p.r + r0 + rr] = bf16_rne(t);
+    }
   }
 }
 
@@ -229,7 +305,10 @@ sv_status launch_draft_head(const sv_head_args* a, hipStream_t s) {
   p.cand_logits = a->cand_logits;
   if (p.N == 0) return SV_OK;
   const int pos_tiles = (p.N + 15) / 16;
-  hipLaunchKernelGGL(k_head_u, dim3(p.r / 16, pos_tiles), dim3(64 * kUWaves), 0, s, p);
+  if (p.N <= kUSmallN)
+    hipLaunchKernelGGL(k_head_u_small, dim3(p.r / kURows), dim3(kUThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_head_u, dim3(p.r / 16, pos_tiles), dim3(64 * kUWaves), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) { set_error("draft head stage 1 launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
   hipLaunchKernelGGL(k_head_topk, dim3(p.n_tiles, pos_tiles), dim3(64 * kTopkWaves), 0, s, p);
