@@ -30,6 +30,29 @@ def test_verify_step_workloads(cfg):
     _step(inst, cfg)
 
 
+def test_verify_step_headline_sampled():
+    """The call the benchmark times, at its size: sv_verify_step on the
+    32-sequence 70B-shaped workload (the same launch plan), every sequence's
+    accept results and six sampled (sequence, query head) attention units
+    against the oracle."""
+    need_gpu()
+    spec = dict(next(c for c in CONFIGS if c["name"] == "tree64_llama70b_b32"))
+    inst = make_instance(spec, 0)
+    rng = np.random.default_rng(5)
+    units = {(0, 0), (inst.B - 1, inst.Hq - 1)}
+    while len(units) < 6:
+        units.add((int(rng.integers(0, inst.B)), int(rng.integers(0, inst.Hq))))
+    units = sorted(units)
+    say(f"verify_step headline B={inst.B} T_max={inst.T_max} V={inst.V} units={units}")
+    dev = sv_problem(inst)
+    dev.verify_step()
+    check_mask(dev, inst)
+    ref = oracle.verify_step(inst, attn_units=units)
+    check_attention(dev.attn_result(), ref["attn"], inst.dtype, rows=units, label="headline")
+    exempt = check_accept(dev.accept_results(), ref["accept"], "headline")
+    say(f"  counts {dev.accept_results()['out_count'].tolist()} exempt {exempt}")
+
+
 def test_verify_step_mixed_small():
     need_gpu()
     spec = dict(cfg_id=400, B=5, Hq=16, Hkv=2, D=128, dtype="bf16", logit_dtype="bf16",
