@@ -8,17 +8,18 @@
 //   k_row_topk     one workgroup per (sequence, frontier row, 8192-token
 //                  chunk): reads the chunk of the drafter's probability row
 //                  once into registers and checks the range.  In each wave
-//                  the k-th largest of the lanes' maxima bounds the chunk's
-//                  k-th largest value from below (those k maxima are k tokens
-//                  at least that large); the largest of the waves' bounds is
-//                  used, only tokens at or above it are gathered in LDS as
-//                  exact keys and ranked (when very many tie at that bound, k
-//                  rounds of a block maximum instead).  This is the HBM-bound
-//                  part.
-//   k_expand       one workgroup per sequence: merges the chunks' keys of each
-//                  frontier row, appends the children (value = parent value x
-//                  probability, one float32 multiply) and ranks the new layer
-//                  to pick the next frontier.
+//                  the k-th largest of the lanes' maxima (found by bisection
+//                  on its bits) bounds the chunk's k-th largest value from
+//                  below (those k maxima are k tokens at least that large);
+//                  the largest of the waves' bounds is used, only tokens at or
+//                  above it are gathered in LDS as exact keys and ranked (when
+//                  very many tie at that bound, k rounds of a block maximum
+//                  over the chunk read again).  This is the HBM-bound part.
+//   k_expand       one workgroup per sequence: merges each frontier row's
+//                  chunk lists (sorted, so a k-way merge by DPP maxima),
+//                  appends the children (value = parent value x probability,
+//                  one float32 multiply) and ranks the new layer to pick the
+//                  next frontier.
 //   k_finish       one workgroup per sequence: ranks every draft node, keeps
 //                  the m best and assigns flattened positions depth by depth.
 //
