@@ -333,6 +333,46 @@ def cpu_baseline(inst, seconds):
                       f"{dt:.1f} s, scaled to the batch"}
 
 
+def all_workloads(steps):
+    """One line per workload: the verify step (median of single steps between
+    HIP events), attention and accept launches timed apart, attention against
+    the bf16 MFMA peak (the fp32 workload against the fp32 vector peak) and
+    HBM, and the walk against reading every tree row's logits once at peak."""
+    import numpy as np
+    import torch
+    import eagle_tree_verification_attn_amd as sv
+    from eagle_tree_verification_attn_amd.problem import DeviceProblem
+    from synth import CONFIGS, make_instance
+    sv.lib()
+    stream = torch.cuda.current_stream()
+    for cfg in CONFIGS:
+        inst = make_instance(cfg, 0)
+        dev = DeviceProblem(inst, device="cuda:0")
+        for _ in range(5):
+            dev.verify_step()
+        torch.cuda.synchronize()
+        step = step_distribution(dev, steps, stream)
+        attn_ms = time_launches(dev.tree_attn, steps, stream)
+        acc_ms = time_launches(dev.spec_accept, steps, stream)
+        res = dev.accept_results()
+        flops, attn_bytes = algorithmic_work(inst)
+        peak = MFMA_BF16_PEAK_TFLOPS if inst.dtype == "bf16" else 157.3
+        sz = 2 if inst.logit_dtype == "bf16" else 4
+        every_row_ms = sz * inst.V * float(inst.num_nodes.sum()) / (HBM_PEAK_GBS * 1e9) * 1e3
+        print(json.dumps({
+            "workload": cfg["name"], "step_median_ms": step["median_ms"],
+            "steps_per_s": round(1e3 / step["median_ms"], 1),
+            "tree_attn_ms": round(attn_ms, 5), "spec_accept_ms": round(acc_ms, 5),
+            "attn_TFLOP_s": round(flops / (attn_ms * 1e-3) / 1e12, 2),
+            "attn_frac_of_peak": round(flops / (attn_ms * 1e-3) / 1e12 / peak, 4),
+            "attn_peak_TFLOP_s": peak,
+            "attn_frac_hbm": round(attn_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "walk_vs_every_row_once": round(acc_ms / every_row_ms, 3),
+            "emitted_per_seq": round(float(np.mean(res["out_count"])), 3)}), flush=True)
+        del dev, inst
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,9 +384,14 @@ def main():
     ap.add_argument("--kernels-only", action="store_true",
                     help="launch the kernels a few times plus a 1 GiB copy (for rocprofv3)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="time the verify step of every workload (one JSON line each), not the headline line")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.all_workloads:
+        all_workloads(args.steps)
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
