@@ -735,14 +735,19 @@ sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_
   // about 20 us more per call.)  Workgroups queued behind other work on the
   // device start when that work ends; the waits are bounded by time and
   // report SV_TREE_E_SYNC rather than hang.
-  static int occ_cache[64][4];   // per device and kernel variant, 0 = not asked yet
+  // per device and kernel variant, 0 = not asked yet (the same value whichever thread fills it)
+  static std::atomic<int> occ_cache[64][4];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int& occ = occ_cache[dev][(wp.bf16 ? 2 : 0) + (vec ? 1 : 0)];
+  std::atomic<int>& slot = occ_cache[dev][(wp.bf16 ? 2 : 0) + (vec ? 1 : 0)];
+  int occ = slot.load(std::memory_order_relaxed);
   if (e == hipSuccess && occ == 0) {
     // the smallest chunk size needs the least LDS: ask with the largest
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAccThreads, 2 * kMaxChunk * sizeof(float));
-    if (e == hipSuccess && occ == 0) occ = -1;
+    if (e == hipSuccess) {
+      if (occ == 0) occ = -1;
+      slot.store(occ, std::memory_order_relaxed);
+    }
   }
   if (e == hipSuccess && (occ < 1 || pl.ngroups * pl.nchunk > device_info().num_cu)) {
     set_error("accept walk: %d workgroups do not fit at once (%d per CU, %d CUs)", pl.ngroups * pl.nchunk, occ,

@@ -704,7 +704,7 @@ size_t smem_bytes(int D, int T_max) {
 // Workgroups of one MFMA variant resident per CU (occupancy query, cached per
 // device and variant; 2 when the runtime cannot tell).
 int resident_groups(int D, int nt, int nw, size_t smem) {
-  static int cache[64][16];
+  static std::atomic<int> cache[64][16];   // the same value whichever thread fills it
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   int idx = -1, i = 0;
@@ -713,13 +713,13 @@ int resident_groups(int D, int nt, int nw, size_t smem) {
     ++i;
   }
   if (idx < 0) return 2;
-  if (cache[dev][idx] == 0) {
+  int n = cache[dev][idx].load(std::memory_order_relaxed);
+  if (n == 0) {
     const void* fn = variant_kernel(D, nt, nw);
-    int n = 0;
     if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, nw * 64, smem) != hipSuccess || n < 1) n = 2;
-    cache[dev][idx] = n;
+    cache[dev][idx].store(n, std::memory_order_relaxed);
   }
-  return cache[dev][idx];
+  return n;
 }
 
 bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* pl) {
@@ -808,13 +808,13 @@ bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* pl) {
 template <int D, int NT, int NW>
 static hipError_t launch_mfma(const AttnParams& prm, int grid, size_t smem, hipStream_t s) {
   auto k = k_attn_bf16<D, NT, NW>;
-  static bool attr_set[64] = {};
+  static std::atomic<bool> attr_set[64];   // setting the attribute twice is harmless
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  if (dev < 64 && !attr_set[dev]) {
+  if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_relaxed)) {
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set[dev] = true;
+    if (dev >= 0 && dev < 64) attr_set[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), smem, s, prm);
   return hipGetLastError();

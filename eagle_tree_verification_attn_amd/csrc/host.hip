@@ -19,19 +19,20 @@ void set_error(const char* fmt, ...) {
 }
 void clear_error() { g_err[0] = 0; }
 
+// Filled once per device; concurrent first calls from several host threads
+// are serialised by the once flag.
 const DeviceInfo& device_info() {
   static DeviceInfo infos[64];
-  static bool have[64];
+  static std::once_flag once[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!have[dev]) {
+  std::call_once(once[dev], [dev] {
     DeviceInfo d{dev, 256, 8};
     int cu = 0;
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
       d.num_cu = cu;
     infos[dev] = d;
-    have[dev] = true;
-  }
+  });
   return infos[dev];
 }
 

@@ -26,7 +26,9 @@
  *    the host (null pointers, bad sizes, a workspace that is too small,
  *    unsupported shapes) are reported before anything is launched; a launch
  *    failure returns SV_E_HIP.  sv_last_error() gives a detail string for the
- *    calling thread.
+ *    calling thread.  Calls may come from several host threads at once; the
+ *    library's only shared host state is a per-device cache of occupancy and
+ *    device facts, filled with atomic stores.
  *  - Problems in the data (a malformed tree, a token outside the vocabulary,
  *    a non-finite target logit) are per sequence: they are reported on the
  *    device in tree_status[b] (SV_TREE_*), and that sequence's outputs are
@@ -176,9 +178,11 @@ sv_status sv_tree_attn(const sv_tree* tree, const uint64_t* anc, const int32_t* 
  *   aligned.  The walk kernel's workgroups (at most one per CU) wait for one
  *   another, so all of them must be resident together: on a device shared with
  *   other work, workgroups queued behind it start when it ends; a wait longer
- *   than 2 s reports SV_TREE_E_SYNC.  Calls that overlap on one device must
- *   use different workspaces.  Returns SV_E_UNSUPPORTED if the grid cannot be
- *   resident at once. */
+ *   than 2 s reports SV_TREE_E_SYNC.  Two walks that overlap on one device
+ *   (calls on different streams) can each take part of the CUs the other's
+ *   groups need, and then both end with SV_TREE_E_SYNC: order walks on one
+ *   device (one stream, or events between streams).  Returns
+ *   SV_E_UNSUPPORTED if the grid cannot be resident at once. */
 sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_accept_args* a,
                          void* ws, size_t ws_bytes, void* stream);
 
@@ -187,7 +191,8 @@ sv_status sv_spec_accept(const sv_tree* tree, int32_t* tree_status, const sv_acc
  * sv_workspace_bytes(tree, attn, acc) bytes: the attention's partial results
  * first, then the accept's exchange words, which the mask kernel zeroes (so
  * the step launches three kernels).  Results are those of the three calls
- * made one after another. */
+ * made one after another; the walk's rule on overlapping calls applies to
+ * steps too. */
 sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
                          uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws,
                          size_t ws_bytes, void* stream);

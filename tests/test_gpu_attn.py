@@ -136,3 +136,51 @@ def test_attention_full_workloads_sampled(cfg):
     inst = make_instance(spec, 0, with_accept=False)
     rows = None if spec["cfg_id"] == 1 else _sample_units(inst)
     _run(inst, f"full {cfg}", rows=rows)
+
+
+def test_attention_from_host_threads():
+    """Four host threads, each with its own stream, workspace and outputs, run
+    the mask and the attention at the same time; each result equals the one
+    the same problem gives in a serial call, bit for bit."""
+    need_gpu()
+    import threading
+
+    import torch
+    specs = [_spec(B=3, Hq=16, Hkv=2, prefix_len=[0, 77, 300], tree=("dynamic", 1, 5, 1, 6, 1, 40), T_max=48),
+             _spec(B=3, Hq=16, Hkv=2, D=64, prefix_len=[513, 64, 1], tree=("dynamic", 1, 6, 1, 8, 1, 60)),
+             _spec(B=2, Hq=8, Hkv=8, prefix_len=[1000, 129]),
+             _spec(B=4, Hq=16, Hkv=2, prefix_len=[2048, 5, 640, 0])]
+    insts = [make_instance(s, 10 + i, with_accept=False) for i, s in enumerate(specs)]
+    say("attn host threads: serial reference calls")
+    serial = []
+    for inst in insts:
+        dev = sv_problem(inst, with_accept=False)
+        dev.mask_build()
+        dev.tree_attn()
+        serial.append(dev.out.clone())
+    torch.cuda.synchronize()
+    devs = [sv_problem(inst, with_accept=False) for inst in insts]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            for _ in range(5):
+                devs[i].mask_build(stream=s)
+                devs[i].tree_attn(stream=s)
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(f"thread {i}: {e}")
+
+    say("attn host threads: 4 threads x 5 calls")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(devs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i, dev in enumerate(devs):
+        assert torch.equal(dev.out, serial[i]), f"problem {i} differs from its serial result"
