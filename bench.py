@@ -96,15 +96,24 @@ def time_launches(fn, n, stream):
     return a.elapsed_time(b) / n
 
 
+def attn_build_hash():
+    """sha256 of the attention source and the compiler flags it is built with
+    (include paths left out, since they name the checkout's location)."""
+    from eagle_tree_verification_attn_amd import build as B
+    flags = [f for f in B.CFLAGS + B.FILE_FLAGS.get("attn.hip", []) if f != "-I" and os.sep not in f]
+    h = hashlib.sha256(open(ATTN_SRC, "rb").read())
+    h.update(" ".join(flags).encode())
+    return h.hexdigest()
+
+
 def counters_traffic():
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+    summary, if it was taken on the current kernel source and flags; else None."""
     if not os.path.exists(COUNTERS):
         return None
     try:
         info = json.load(open(COUNTERS))
-        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if info.get("attn_source_sha256") != src:
+        if info.get("attn_build_sha256") != attn_build_hash():
             return None
         return float(info["hbm_bytes_per_launch"])
     except Exception:
@@ -138,7 +147,7 @@ def summarize_counters(fetch_csv, write_csv):
     hbm = 1024.0 * (fa * f_factor + wa * w_factor)
     out = {
         "kernel": f"{ATTN_KERNEL} (sv_tree_attn), workload {WORKLOAD}",
-        "attn_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+        "attn_build_sha256": attn_build_hash(),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch --output-format csv "
             "-- python3 bench.py --kernels-only",

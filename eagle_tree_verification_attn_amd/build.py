@@ -28,8 +28,11 @@ CFLAGS = [
 
 
 # Per-file flags.  attn.hip: scores are finite or -inf (masked), never NaN by
-# construction of the kernel, so max needs no NaN canonicalisation.
-FILE_FLAGS = {"attn.hip": ["-fno-honor-nans"]}
+# construction of the kernel, so max needs no NaN canonicalisation; the
+# scheduler's AMDGPU register-pressure trackers give the attention kernels a
+# schedule measured about 2% faster on gfx950, with the same registers and
+# bit-identical results.
+FILE_FLAGS = {"attn.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-use-amdgpu-trackers=1"]}
 
 
 def _compile(src):
