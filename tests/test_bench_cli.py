@@ -47,3 +47,16 @@ def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
     assert abs(d["fetch_scale"] - 2.0) < 1e-9 and abs(d["write_scale"] - 1.0) < 1e-9
     want = 1024 * (510000.0 * 2.0 + 32000.0 * 1.0)
     assert abs(d["hbm_bytes_per_launch"] - want) < 1.0
+
+
+def test_counter_hash_tracks_flags_not_location(monkeypatch):
+    """The counter summary is keyed by the attention source and its compiler
+    flags: another flag changes the key, another checkout location does not."""
+    import bench
+    from eagle_tree_verification_attn_amd import build as B
+    h0 = bench.attn_build_hash()
+    moved = [("/elsewhere/include" if os.sep in f else f) for f in B.CFLAGS]
+    monkeypatch.setattr(B, "CFLAGS", moved)
+    assert bench.attn_build_hash() == h0
+    monkeypatch.setattr(B, "FILE_FLAGS", {"attn.hip": B.FILE_FLAGS["attn.hip"] + ["-O2"]})
+    assert bench.attn_build_hash() != h0
