@@ -162,3 +162,36 @@ def test_accept_full_workloads(cfg):
     inst = make_instance(spec, 0, with_attn=False)
     res, ref, exempt = _run(inst, f"full {cfg}")
     say(f"  counts {res['out_count'].tolist()} passes {res['out_passes'].tolist()} exempt {exempt}")
+
+
+def test_accept_on_two_streams_ordered_by_events():
+    """Walks on two streams, each ordered after the other's previous walk by an
+    event (the rule for walks on one device), give the results of serial calls."""
+    need_gpu()
+    import torch
+    insts = [make_instance(_spec(cfg_id=223, B=16, V=20000, tau=0.9), s, with_attn=False) for s in (3, 4)]
+    say("accept two streams with events")
+    serial = []
+    for inst in insts:
+        dev = sv_problem(inst, with_attn=False)
+        dev.mask_build()
+        dev.spec_accept()
+        serial.append(dev.accept_results())
+    devs = [sv_problem(inst, with_attn=False) for inst in insts]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    done = None
+    for r in range(4):
+        i = r % 2
+        s = streams[i]
+        devs[i].mask_build(stream=s)
+        if done is not None:
+            s.wait_event(done)
+        devs[i].spec_accept(stream=s)
+        done = torch.cuda.Event()
+        done.record(s)
+    torch.cuda.synchronize()
+    for i, dev in enumerate(devs):
+        got = dev.accept_results()
+        for k in ("out_nodes", "out_tokens", "out_count", "out_passes"):
+            np.testing.assert_array_equal(got[k], serial[i][k])
