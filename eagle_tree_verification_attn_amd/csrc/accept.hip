@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
         tok_s[i] = x;
         ua_s[i] = p.u_accept[rowbase + i];
         us_s[i] = p.u_sample[rowbase + i];
-        if (x < 0 || x >= p.V) atomicOr(&flags_s, 1);
+        if (i > 0 && (x < 0 || x >= p.V)) atomicOr(&flags_s, 1);   // the root's token is not read
       }
       __syncthreads();
       if (flags_s & 1) st = SV_TREE_E_TOKEN;

@@ -69,7 +69,7 @@ enum {
   SV_TREE_E_ROOT = 1,      /* parent[b][0] != -1                                      */
   SV_TREE_E_PARENT = 2,    /* some 1 <= i < T_b has parent[b][i] outside [0, i)       */
   SV_TREE_E_COUNT = 3,     /* num_nodes[b] outside [1, T_max]                         */
-  SV_TREE_E_TOKEN = 4,     /* some tokens[b][i], i < T_b, outside [0, V)              */
+  SV_TREE_E_TOKEN = 4,     /* a draft token tokens[b][i], 1 <= i < T_b, outside [0, V) */
   SV_TREE_E_NONFINITE = 5, /* a NaN or +-Inf in the logits row of a node the walk visits */
   SV_TREE_E_NOQ = 6,       /* temperature[b] > 0 but q_probs is NULL                  */
   SV_TREE_E_SYNC = 7,      /* internal: a cross-workgroup wait timed out              */
@@ -91,7 +91,8 @@ typedef struct {
   int32_t T_max;            /* padded positions per sequence (root + draft nodes)     */
   const int32_t* parent;    /* [B][T_max]; parent[b][0] = -1, 0 <= parent[b][i] < i   */
   const int32_t* num_nodes; /* [B]; T_b = root + draft nodes, 1 <= T_b <= T_max       */
-  const int32_t* tokens;    /* [B][T_max]; token of each position (root's is unused)  */
+  const int32_t* tokens;    /* [B][T_max]; token of each position; the root's (position
+                               0) is never read, draft tokens must be in [0, V)       */
 } sv_tree;
 
 /* Tree attention inputs (post-RoPE projections of one layer). */

@@ -29,10 +29,11 @@ in the design notes of the repository):
   earlier siblings' tokens removed and renormalised when siblings were drawn
   without replacement, and q itself when drawn i.i.d.;
 * the terminal draw is an inverse CDF in ascending token order;
-* a token outside [0, V), a stochastic sequence without draft probabilities,
-  or a non-finite target logit in a row the walk reads (the row of every node
-  it visits) marks the sequence invalid (count 0, outputs -1); rows of nodes
-  the walk never reaches are not inspected.
+* a draft token (position 1 .. T_b-1) outside [0, V), a stochastic sequence
+  without draft probabilities, or a non-finite target logit in a row the walk
+  reads (the row of every node it visits) marks the sequence invalid (count 0,
+  outputs -1); rows of nodes the walk never reaches are not inspected, and the
+  root's token (the last emitted token, never a candidate) is not read.
 
 Parity is pinned by the tests under ``tests/test_oracle_*.py`` (closed forms,
 the worked example trees and numbers the pages print, library routines for the
@@ -172,12 +173,15 @@ def tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len, anc, num_nodes
         Kt = to_f64(k_new[b, :T_b], dtype)        # T_b x Hkv x D
         Vt = to_f64(v_new[b, :T_b], dtype)
         visible = np.concatenate([np.ones((T_b, L_b), dtype=bool), anc[b, :T_b, :T_b]], axis=1)
+        kv_rows = {}   # KV head -> its keys and values, widened once for its query heads
         for h in heads:
             kv = h // G
-            Kp = to_f64(k_cache[b, kv, :L_b], dtype)   # L_b x D
-            Vp = to_f64(v_cache[b, kv, :L_b], dtype)
-            Kall = np.concatenate([Kp, Kt[:, kv]], axis=0)   # (L_b + T_b) x D
-            Vall = np.concatenate([Vp, Vt[:, kv]], axis=0)
+            if kv not in kv_rows:
+                Kp = to_f64(k_cache[b, kv, :L_b], dtype)   # L_b x D
+                Vp = to_f64(v_cache[b, kv, :L_b], dtype)
+                kv_rows = {kv: (np.concatenate([Kp, Kt[:, kv]], axis=0),    # (L_b + T_b) x D
+                                np.concatenate([Vp, Vt[:, kv]], axis=0))}
+            Kall, Vall = kv_rows[kv]
             S = s * (Q[:, h] @ Kall.T)                      # T_b x (L_b + T_b)
             S = np.where(visible, S, -np.inf)
             S = S - S.max(axis=1, keepdims=True)
@@ -343,7 +347,7 @@ def spec_accept(parent, num_nodes, tokens, target_logits, logit_dtype, q_probs, 
         if status[b] != TREE_OK:
             continue
         T_b = int(num_nodes[b])
-        tk = np.asarray(tokens[b, :T_b], dtype=np.int64)
+        tk = np.asarray(tokens[b, 1:T_b], dtype=np.int64)   # draft tokens; the root's is not a candidate
         if np.any(tk < 0) or np.any(tk >= V):
             status[b] = TREE_E_TOKEN
             continue

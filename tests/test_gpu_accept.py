@@ -99,7 +99,7 @@ def test_accept_malformed_inputs():
     assert unvisited7, "sequence 7 must have a node the walk skips"
     inst.parent[0, 1] = 3                         # tree error
     inst.tokens[1, 1] = inst.V                    # token out of range
-    inst.tokens[2, 0] = -1                        # root token out of range
+    inst.tokens[2, 0] = -1                        # the root's token is never read
     bits = {"nan": 0x7FC0, "inf": 0x7F80, "-inf": 0xFF80}
     inst.target_logits[3, 0, 17] = bits["nan"]                       # the root row is always read
     inst.target_logits[4, int(inst.num_nodes[4]) - 1, 5] = bits["inf"]  # read only if visited
@@ -109,8 +109,9 @@ def test_accept_malformed_inputs():
         inst.target_logits[6, inst.T_max - 1, 3] = bits["nan"]
     inst.target_logits[7, unvisited7[-1], 11] = bits["nan"]          # a row the walk never reads
     res, ref, _ = _run(inst, "malformed")
-    assert res["status"][:4].tolist() == [oracle.TREE_E_PARENT, oracle.TREE_E_TOKEN, oracle.TREE_E_TOKEN,
+    assert res["status"][:4].tolist() == [oracle.TREE_E_PARENT, oracle.TREE_E_TOKEN, oracle.TREE_OK,
                                           oracle.TREE_E_NONFINITE]
+    np.testing.assert_array_equal(res["out_tokens"][2], clean["out_tokens"][2])
     assert res["status"][5] == oracle.TREE_E_NONFINITE
     assert res["status"][4] == ref["status"][4]
     assert res["status"][6] == 0 and res["status"][7] == 0

@@ -13,6 +13,8 @@
   detectably biased;
 * residual law: after a rejection, the correction is distributed as
   (p - q)+ normalised;
+* input rules: draft tokens in [0, V) (the root's token unread), draft
+  probabilities required at temperature > 0 only;
 * special cases: q = p always accepts; p(x) = 0 always rejects; one-hot p and
   q reproduce the greedy walk.
 """
@@ -329,3 +331,73 @@ def test_nonfinite_logits_only_in_rows_the_walk_reads(row, bad):
     else:
         assert res["status"][0] == oracle.TREE_E_NONFINITE
         assert res["out_count"][0] == 0 and (res["out_nodes"] == -1).all()
+
+
+def _spec_accept_one(parent, tokens, z, q, tau, ua, us):
+    num = np.array([parent.shape[1]], dtype=np.int32)
+    return oracle.spec_accept(parent, num, tokens, z, "f32", q, np.array([tau], np.float32), ua, us,
+                              np.zeros(1, np.int32), IID)
+
+
+@pytest.mark.parametrize("pos,value,want", [
+    (1, 12, oracle.TREE_E_TOKEN),    # = V: one past the last vocabulary id
+    (3, 12, oracle.TREE_E_TOKEN),    # a deeper node
+    (2, -1, oracle.TREE_E_TOKEN),    # negative, on a node the walk never visits
+    (1, 11, oracle.TREE_OK),         # V - 1: the last valid id
+    (1, 0, oracle.TREE_OK),          # the first valid id
+    (0, -7, oracle.TREE_OK),         # the root's token: never a candidate, not read
+    (0, 12, oracle.TREE_OK),
+])
+def test_token_range_rule(pos, value, want):
+    """A draft token indexes the vocabulary rows p and q (the lesson's
+    "Exactness rule" reads p(x) and q(x)), so every draft token must lie in
+    [0, V); one outside makes the sequence invalid with count 0 and -1
+    outputs, wherever the node sits in the tree.  The root is the last
+    emitted token, not a candidate, so its token is not checked."""
+    parent, z, q, tokens, ua, us = _two_child_tree_instance(V=12)
+    tokens = tokens.copy()
+    tokens[0, pos] = value
+    res = _spec_accept_one(parent, tokens, z, q, 1.0, ua, us)
+    assert res["status"][0] == want
+    if want == oracle.TREE_OK:
+        if pos == 0:   # the outcome does not depend on the root's token
+            clean = _spec_accept_one(parent, _two_child_tree_instance(V=12)[3], z, q, 1.0, ua, us)
+            np.testing.assert_array_equal(res["out_tokens"], clean["out_tokens"])
+        assert res["out_count"][0] >= 1
+    else:
+        assert res["out_count"][0] == 0 and (res["out_nodes"] == -1).all() and (res["out_tokens"] == -1).all()
+        assert res["walks"][0] is None
+
+
+@pytest.mark.parametrize("tau,want", [(1.0, oracle.TREE_E_NOQ), (0.25, oracle.TREE_E_NOQ),
+                                      (0.0, oracle.TREE_OK), (-1.0, oracle.TREE_OK)])
+def test_missing_q_rule(tau, want):
+    """Stochastic verification divides by q(x) (the lesson's "Exactness
+    rule"), so a sequence at temperature > 0 without draft probabilities is
+    invalid; greedy verification compares with argmax p only and needs no q,
+    and then gives the same result as with q present."""
+    parent, z, q, tokens, ua, us = _two_child_tree_instance(V=12)
+    res = _spec_accept_one(parent, tokens, z, None, tau, ua, us)
+    assert res["status"][0] == want
+    if want == oracle.TREE_E_NOQ:
+        assert res["out_count"][0] == 0 and (res["out_nodes"] == -1).all() and (res["out_tokens"] == -1).all()
+    else:
+        with_q = _spec_accept_one(parent, tokens, z, q, tau, ua, us)
+        np.testing.assert_array_equal(res["out_tokens"], with_q["out_tokens"])
+        np.testing.assert_array_equal(res["out_nodes"], with_q["out_nodes"])
+        # the emitted token is the argmax of the last visited node's row
+        last = 0 if res["out_count"][0] == 1 else int(res["out_nodes"][0, res["out_count"][0] - 2])
+        assert res["out_tokens"][0, res["out_count"][0] - 1] == int(np.argmax(z[0, last]))
+
+
+def test_missing_q_rule_per_sequence():
+    """The rule is per sequence: in a batch with mixed temperatures and no q,
+    only the stochastic sequences are invalid."""
+    parent, z, q, tokens, ua, us = _two_child_tree_instance(V=12)
+    B = 4
+    P = np.repeat(parent, B, 0)
+    res = oracle.spec_accept(P, np.full(B, 4, np.int32), np.repeat(tokens, B, 0), np.repeat(z, B, 0), "f32", None,
+                             np.array([0.0, 1.0, 0.0, 0.7], np.float32), np.repeat(ua, B, 0),
+                             np.repeat(us, B, 0), np.zeros(B, np.int32), IID)
+    assert res["status"].tolist() == [oracle.TREE_OK, oracle.TREE_E_NOQ, oracle.TREE_OK, oracle.TREE_E_NOQ]
+    assert res["out_count"].tolist()[1::2] == [0, 0]
