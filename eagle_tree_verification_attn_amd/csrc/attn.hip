@@ -14,9 +14,11 @@
 //
 //   scores   S^T[key][row] = K[key] . Q[row]     v_mfma_f32_16x16x32_bf16,
 //            A = K rows from LDS, B = Q held in registers for the whole run;
-//   softmax  online, fp32, exp2 with the scale folded in; the running max is
-//            only raised when a block's max exceeds it by more than 8 (log2
-//            units), so the O rescale is rare and exp2 arguments stay <= 8;
+//   softmax  online, fp32: the MFMA yields raw dot products of the bf16 q and
+//            k as stored, and the score scale times log2(e) is applied to them
+//            in fp32 right before exp2; the running max is only raised when a
+//            block's max exceeds it by more than 8 (log2 units), so the O
+//            rescale is rare and exp2 arguments stay <= 8;
 //   output   O^T[d][row] += V^T[d][key] P^T[key][row]: B = P taken straight
 //            from the score registers; A = V^T read from the row-major V tile
 //            with ds_read_b64_tr_b16 (each 16-lane group gathers 4 keys x 16
@@ -53,7 +55,8 @@ struct AttnParams {
   int B, T_max, Hq, Hkv, G, L_max, W;
   int rows_per_wg, msplit, lsplit, chunk;
   int remap;
-  float scale_log2;
+  float scale_log2;  // score scale * log2(e), applied in fp32
+  float raise_raw;   // 8 / scale_log2: the offset-raise bound in raw dot-product units
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block i runs on XCD
@@ -102,11 +105,11 @@ __device__ inline bf16x4 lds_read_tr16(const __bf16* p) {
 // i of the wave writes LDS bytes [m0 + 16 i, m0 + 16 i + 16).  Issued as
 // inline asm so that the compiler's wait-count bookkeeping (which would wait
 // for every outstanding copy before any LDS read) stays out of the pipeline;
-// the kernel waits for its copies itself with s_waitcnt vmcnt.  m0 is only
-// ever set right here.
+// the kernel waits for its copies itself with s_waitcnt vmcnt.  The asm sets
+// m0 and says so, so the compiler keeps nothing of its own in m0 across it.
 __device__ inline void copy16_to_lds(const void* gptr, uint32_t lds_byte_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr)) : "memory");
+               :: "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr)) : "memory", "m0");
 }
 // Wait until at most N of this wave's vector-memory loads are outstanding
 // (they complete in issue order), then join the workgroup barrier.
@@ -233,10 +236,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int W = p.W;
   for (int i = tid; i < p.T_max * W; i += NTHR) anc_s[i] = p.anc[(size_t)b * p.T_max * W + i];
 
-  // queries -> registers (B operand of the score MFMA), multiplied by
-  // scale * log2(e) and rounded to bf16 once, so the MFMA yields scores in
-  // log2 units (relative error 2^-9 per element of q: about 0.1% on p for
-  // unit-variance data, below the bf16 rounding of p itself)
+  // queries -> registers (B operand of the score MFMA) exactly as stored: the
+  // score MFMA then yields raw dot products with fp32 accumulation, and the
+  // scale is applied to those in fp32.  (Rounding scale * log2(e) * q to bf16
+  // instead would put a relative error of 2^-9 on every product, an exponent
+  // error that grows with the score: at score spreads of a peaked softmax it
+  // moves weights by several percent.)
   bf16x8 qreg[NT][DK];
 #pragma unroll
   for (int qt = 0; qt < NT; ++qt) {
@@ -245,14 +250,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int t = r / G, h = kvh * G + r % G;
       const __bf16* src = qp + (((size_t)b * p.T_max + t) * p.Hq + h) * D + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 32 * kk);
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = pack_bf16x2((float)x[2 * e] * p.scale_log2, (float)x[2 * e + 1] * p.scale_log2);
-        qreg[qt][kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-      }
+      for (int kk = 0; kk < DK; ++kk) qreg[qt][kk] = *reinterpret_cast<const bf16x8*>(src + 32 * kk);
     } else {
 #pragma unroll
       for (int kk = 0; kk < DK; ++kk) qreg[qt][kk] = bf16x8{};
@@ -261,9 +259,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // acc: O^T tiles; lsum: the row sums of P, accumulated by an MFMA with an
   // all-ones A operand, so every element of lsum[qt] holds its column's sum.
-  // mu: the running exp2 offset of the lane's row (log2 units), subtracted by
-  // the score MFMA itself (its accumulator starts at cinit = -mu); valid once
-  // a visible key has set it.  P = 2^(score - mu) with score - mu <= 8 kept.
+  // mu: the running offset of the lane's row in raw dot-product units,
+  // subtracted by the score MFMA itself (its accumulator starts at
+  // cinit = -mu); valid once a visible key has set it.  With c = scale *
+  // log2(e), P = 2^(c (dot - mu)) with c (dot - mu) <= 8 kept.
   f32x4 acc[NT][DT], lsum[NT], cinit[NT];
   float mu[NT];
   bool valid[NT];
@@ -401,9 +400,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // ---- online softmax of s, P packed to bf16 for the PV MFMA and kept in the
   // registers of s[qt][0] (so only s lives from one phase to the next).  The
-  // scores already are score - mu in log2 units.  Each lane compares the
-  // maximum of its values with the bound 8; only when some lane exceeds it, or
-  // a row has no offset yet, does the wave form column maxima and raise offsets.
+  // scores already are dot - mu (raw units).  Each lane compares the maximum
+  // of its values with the bound 8 / c; only when some lane exceeds it, or a
+  // row has no offset yet, does the wave form column maxima and raise offsets.
+  const float c2 = p.scale_log2, thr = p.raise_raw;
   auto softmax = [&]() {
     float pmax = -INFINITY;
     bool unset = false;
@@ -413,18 +413,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                                fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]))));
       unset |= !valid[qt];
     }
-    if (__any(pmax > 8.0f || unset)) {
+    if (__any(pmax > thr || unset)) {
 #pragma unroll
       for (int qt = 0; qt < NT; ++qt) {
         const float a0 = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
         const float a1 = fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]));
-        const float cm = col_max4(fmaxf(a0, a1));   // column max of score - mu
+        const float cm = col_max4(fmaxf(a0, a1));   // column max of dot - mu
         // a row without an offset takes the first visible maximum (its
-        // accumulators are still zero); a row with one raises it past 8
-        const bool raise = valid[qt] ? cm > 8.0f : cm > -INFINITY;
+        // accumulators are still zero); a row with one raises it past 8 / c
+        const bool raise = valid[qt] ? cm > thr : cm > -INFINITY;
         if (raise) {
           if (valid[qt]) {
-            const float alpha = __builtin_amdgcn_exp2f(-cm);
+            const float alpha = __builtin_amdgcn_exp2f(-cm * c2);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
             lsum[qt] *= alpha;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[kt * 4 + i] = __builtin_amdgcn_exp2f(s[qt][kt][i]);
+        for (int i = 0; i < 4; ++i) pv[kt * 4 + i] = __builtin_amdgcn_exp2f(s[qt][kt][i] * c2);
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             make_float4(acc[qt][dt][0], acc[qt][dt][1], acc[qt][dt][2], acc[qt][dt][3]);
       if (g == 0) {
         float* pm = p.part_ml + (orow * p.lsplit + ls_i) * 2;
-        pm[0] = valid[qt] ? mu[qt] : -INFINITY;
+        pm[0] = valid[qt] ? mu[qt] * c2 : -INFINITY;   // log2 units for the merge
         pm[1] = l;
       }
     }
@@ -847,6 +847,7 @@ sv_status launch_attention(const sv_tree* t, const uint64_t* anc, const int32_t*
   prm.chunk = pl.chunk;
   const double scale = a->scale > 0.f ? (double)a->scale : 1.0 / sqrt((double)a->D);
   prm.scale_log2 = (float)(scale * 1.4426950408889634);
+  prm.raise_raw = 8.f / prm.scale_log2;
   if (pl.lsplit > 1) {
     const size_t rows = (size_t)t->B * t->T_max * a->Hq * pl.lsplit;
     prm.part_o = reinterpret_cast<float*>(ws);

@@ -17,7 +17,15 @@ Recipe (one instance per (spec, seed)):
   q row of that node, without replacement ("wor") or i.i.d. ("iid"); for a
   greedy sequence they are the top-k of z_q (ties to the lowest index).  The root
   token is uniform over the vocabulary.
-* Attention inputs q, k_new, v_new, k_cache, v_cache ~ N(0, 1), cast to ``dtype``.
+* Attention inputs q, k_new, v_new, k_cache, v_cache ~ N(0, 1), cast to ``dtype``;
+  with ``qk_std`` = s the queries and keys are N(0, s^2) instead (score spread
+  s^2 in natural units: a peaked softmax, as in a trained target's forward).
+* ``plant`` = g (optional): every query row (sequence, position t < T_b, query
+  head) gets one dominant key.  From its own Philox stream, each row picks
+  the key of its own tree node, of its parent node (t > 0), or a uniform
+  prefix key (L_b > 0), each allowed choice equally likely, and adds
+  gamma * key to the query with gamma = g * qk_std^2 * sqrt(D) / |key|^2, so
+  that this key's scaled score exceeds the random part by g * qk_std^2.
 * Uniforms ``u_accept``, ``u_sample`` ~ U[0, 1) float32.
 
 Padding rows (node index >= T_b) are filled too (random values, parent -1,
@@ -145,6 +153,34 @@ def _draw_children(qrow64, k, mode, rng):
     return out
 
 
+def _plant_keys(inst, b, Tb, gain, qk_std, rng):
+    """Give every query row of sequence b (positions t < Tb) one dominant key
+    (see the module docstring): its own tree node's key, its parent's, or a
+    prefix key."""
+    Lb = int(inst.prefix_len[b])
+    G = inst.Hq // inst.Hkv
+    D = inst.D
+    widen = (lambda a: f32_from_bf16_bits(a)) if inst.dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+    q = widen(inst.q[b]).copy()
+    k_new = widen(inst.k_new[b])
+    k_cache = widen(inst.k_cache[b])
+    for t in range(Tb):
+        for h in range(inst.Hq):
+            kv = h // G
+            choices = ["self"] + (["parent"] if t > 0 else []) + (["prefix"] if Lb > 0 else [])
+            pick = choices[int(rng.integers(0, len(choices)))]
+            if pick == "self":
+                key = k_new[t, kv]
+            elif pick == "parent":
+                key = k_new[int(inst.parent[b, t]), kv]
+            else:
+                key = k_cache[kv, int(rng.integers(0, Lb))]
+            n2 = float(np.dot(key.astype(np.float64), key.astype(np.float64)))
+            gamma = gain * qk_std * qk_std * np.sqrt(D) / max(n2, 1e-30)
+            q[t, h] = q[t, h] + np.float32(gamma) * key
+    inst.q[b] = bf16_bits_from_f32(q) if inst.dtype == "bf16" else q
+
+
 def _workers():
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -217,15 +253,20 @@ def make_instance(spec, seed=0, with_attn=True, with_accept=True):
     tokens = np.zeros((B, T_max), dtype=np.int32)
     draft_std = float(s.get("draft_std", 3.0))
     sigma = float(s.get("sigma", 1.0))
+    qk_std = float(s.get("qk_std", 1.0))
+    plant = s.get("plant")
+    r_plant = child(np.random.SeedSequence([cfg_id, int(seed), 7])) if plant else None
 
     def one_sequence(b):
         # ---- attention inputs
         if with_attn:
-            inst.q[b] = _normal(r_qkv[b], (T_max, Hq, D), 1.0, dtype)
-            inst.k_new[b] = _normal(r_qkv[b], (T_max, Hkv, D), 1.0, dtype)
+            inst.q[b] = _normal(r_qkv[b], (T_max, Hq, D), qk_std, dtype)
+            inst.k_new[b] = _normal(r_qkv[b], (T_max, Hkv, D), qk_std, dtype)
             inst.v_new[b] = _normal(r_qkv[b], (T_max, Hkv, D), 1.0, dtype)
-            inst.k_cache[b] = _normal(r_cache[b], (Hkv, L_max, D), 1.0, dtype)
+            inst.k_cache[b] = _normal(r_cache[b], (Hkv, L_max, D), qk_std, dtype)
             inst.v_cache[b] = _normal(r_cache[b], (Hkv, L_max, D), 1.0, dtype)
+            if plant:
+                _plant_keys(inst, b, int(num_nodes[b]), float(plant), qk_std, r_plant[b])
         Tb = int(num_nodes[b])
         rd = r_draft[b]
         if not with_accept:

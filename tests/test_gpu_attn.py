@@ -3,8 +3,12 @@
 Small cases are compared element by element (several key blocks, ragged
 prefixes including 0, ragged trees, T_b = 1, every instantiated kernel shape,
 forced key splits, fp32 and bf16).  The five workload shapes run at full size
-in the launch configuration the benchmark uses and are compared on sampled
-(sequence, head) units the oracle computes one by one.
+in the launch configuration the benchmark uses and are compared on every
+output element.  Peaked inputs (queries and keys with std 2, 3, 4, i.e. score
+spreads of 4 to 16 in natural units, and one planted dominant key per row on
+the row's own tree node, its parent or a prefix key) cover the regime of a
+trained target's forward pass, at a short-prefix shape and at the full
+Llama-3-70B-shaped batch.
 """
 import os
 
@@ -121,21 +125,48 @@ def test_attention_invalid_sequences_zero():
     assert not got[1].any() and not got[2].any()
 
 
-def _sample_units(inst, n=6):
-    rng = np.random.default_rng(0)
-    units = {(0, 0), (inst.B - 1, inst.Hq - 1)}
-    while len(units) < n:
-        units.add((int(rng.integers(0, inst.B)), int(rng.integers(0, inst.Hq))))
-    return sorted(units)
-
-
 @pytest.mark.parametrize("cfg", [c["name"] for c in CONFIGS])
-def test_attention_full_workloads_sampled(cfg):
+def test_attention_full_workloads(cfg):
+    """Every (sequence, position, head) row of each workload at full size."""
     need_gpu()
     spec = dict(next(c for c in CONFIGS if c["name"] == cfg))
     inst = make_instance(spec, 0, with_accept=False)
-    rows = None if spec["cfg_id"] == 1 else _sample_units(inst)
-    _run(inst, f"full {cfg}", rows=rows)
+    _run(inst, f"full {cfg}")
+
+
+@pytest.mark.parametrize("plant", [None, 6.0])
+@pytest.mark.parametrize("qk_std", [2.0, 3.0, 4.0])
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_peaked(D, qk_std, plant):
+    """Large scores: queries and keys N(0, qk_std^2), optionally one planted
+    dominant key per row; ragged prefixes (0 included) and ragged trees."""
+    need_gpu()
+    spec = _spec(B=3, Hq=16, Hkv=2, D=D, prefix_len=[0, 77, 1300], tree=("dynamic", 1, 6, 1, 8, 1, 60),
+                 qk_std=qk_std, plant=plant)
+    inst = make_instance(spec, 21, with_accept=False)
+    _run(inst, f"peaked D={D} std={qk_std} plant={plant}")
+
+
+@pytest.mark.parametrize("lsplit", ["1", "4"])
+def test_attention_peaked_key_splits(lsplit):
+    """Peaked scores with the key range split: the partials' offsets and the
+    merge carry the large exponents."""
+    need_gpu()
+    spec = _spec(B=2, Hq=16, Hkv=2, prefix_len=[2000, 333], tree=("widths", [3, 4, 5]), qk_std=3.0, plant=6.0)
+    inst = make_instance(spec, 22, with_accept=False)
+    _run(inst, f"peaked lsplit={lsplit}", env={"SV_ATTN_LSPLIT": lsplit})
+
+
+def test_attention_peaked_headline():
+    """The Llama-3-70B-shaped batch (32 sequences, 64/8 heads, D = 128, prefix
+    8192, 65 tree positions) with queries and keys of std 3 and a planted key
+    per row (half of them tree keys), in the benchmark's launch plan; every
+    output row compared."""
+    need_gpu()
+    spec = dict(next(c for c in CONFIGS if c["name"] == "tree64_llama70b_b32"))
+    spec.update(qk_std=3.0, plant=6.0)
+    inst = make_instance(spec, 3, with_accept=False)
+    _run(inst, "peaked headline std=3 plant=6")
 
 
 def test_attention_from_host_threads():
