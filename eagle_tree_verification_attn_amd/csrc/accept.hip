@@ -33,6 +33,7 @@
 #include "sv_internal.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace sv {
 
@@ -55,6 +56,7 @@ struct WalkParams {
   int32_t* out_count;
   int32_t* out_passes;
   uint64_t* xchg;  // [ngroups][2][nchunk][kXWords] exchange words, zeroed by k_accept_clear
+  uint64_t wait_ticks;  // bound of one exchange wait, in ticks of the 100 MHz real-time counter
   int B, T_max, V, nchunk, chunk, ngroups;
   int bf16, sibling_mode;
 };
@@ -318,6 +320,7 @@ struct GroupXchg {
   uint64_t* words;  // this group's [2][nchunk][kXWords]
   int nchunk;
   int epoch;
+  uint64_t wait_ticks;
   __device__ uint64_t* slot(int e) const { return words + (size_t)(e & 1) * nchunk * kXWords; }
   // Thread 0 publishes v[0..nv) for workgroup w; threads below nchunk * nv
   // each wait for one member's word and put its value in out[member * nv + j].
@@ -339,17 +342,48 @@ struct GroupXchg {
       const int m = t / nv, j = t % nv;
       uint64_t* wp = sl + (size_t)m * kXWords + j;
       uint64_t x = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // bounded by time (the 100 MHz real-time counter): 2 s
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while ((x >> 32) != (uint64_t)(uint32_t)epoch) {
-        __builtin_amdgcn_s_sleep(1);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull) { ok = 0; break; }
-        x = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (!wait_for(wp, x)) ok = 0;
       out[t] = __uint_as_float((uint32_t)x);
     }
     __syncthreads();
     return ok != 0;
+  }
+  // Polls word wp (already loaded into x) until it carries the current
+  // exchange number; false when the bound (real-time counter ticks) passes.
+  __device__ bool wait_for(uint64_t* wp, uint64_t& x) const {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while ((x >> 32) != (uint64_t)(uint32_t)epoch) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks) return false;
+      x = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return true;
+  }
+  // One-sided exchange: member `from` publishes one value, only member 0
+  // reads it (into *out).  Every member takes the exchange number, so the
+  // group's numbering stays in step.  Returns false (in member 0) when the
+  // wait exceeded its bound.  A slot is still rewritten only two exchanges
+  // later, after a full exchange in between, so the parity rule holds.
+  __device__ bool to_first(int w, int from, uint32_t v, uint32_t* out) {
+    __shared__ int ok1;
+    ++epoch;
+    uint64_t* sl = slot(epoch);
+    if (from == 0) {                     // member 0 has the value itself
+      if (w == 0 && threadIdx.x == 0) *out = v;
+      __syncthreads();
+      return true;
+    }
+    const uint64_t tag = (uint64_t)(uint32_t)epoch << 32;
+    if (w == from && threadIdx.x == 0)
+      __hip_atomic_store(sl + (size_t)from * kXWords, tag | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (w == 0 && threadIdx.x == 0) {
+      uint64_t* wp = sl + (size_t)from * kXWords;
+      uint64_t x = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok1 = wait_for(wp, x) ? 1 : 0;
+      *out = (uint32_t)x;
+    }
+    __syncthreads();
+    return w != 0 || ok1 != 0;
   }
 };
 
@@ -379,6 +413,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
   __shared__ float xv[64 * kXWords];   // the group's exchanged values
   __shared__ float pubv[kXWords];
   __shared__ float bcast, m_b, ls_b, f_b;
+  __shared__ uint32_t tok_b;
   __shared__ int ibcast, am_b, bad_b;
   __shared__ int flags_s;
 
@@ -388,7 +423,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
   const int c0 = w * p.chunk;
   const int c1 = min(c0 + p.chunk, p.V);
   const bool wor = p.sibling_mode == SV_SIB_WITHOUT_REPLACEMENT;
-  GroupXchg gx{p.xchg + (size_t)grp * 2 * p.nchunk * kXWords, p.nchunk, 0};
+  GroupXchg gx{p.xchg + (size_t)grp * 2 * p.nchunk * kXWords, p.nchunk, 0, p.wait_ticks};
   // this workgroup's chunk: e(v) = 2^((z(v) - m_c) k) of the visited node, then q
   extern __shared__ __align__(16) float cache_s[];
   float* pc = cache_s;
@@ -611,8 +646,30 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       }
       break;
     }
+    // the drawn token goes to workgroup 0, which writes every output of the
+    // sequence (one writer per output word, whatever happens to the others)
+    if (sync_ok && !nonfinite && st == SV_TREE_OK && owner != 0) {
+      if (!gx.to_first(w, owner, (uint32_t)emitted, &tok_b)) sync_ok = false;
+      else if (w == 0) emitted = (int)tok_b;
+    }
     if (!sync_ok) {
-      if (tid == 0) p.status[b] = SV_TREE_E_SYNC;
+      // A wait passed its bound (the group's workgroups were not all resident
+      // together): this workgroup stops.  Workgroup 0 marks this sequence and
+      // every later one of the group, which no longer can be walked, with
+      // SV_TREE_E_SYNC (keeping an earlier data status) and -1 / count 0
+      // outputs; it waits for nothing more, so every workgroup ends.
+      if (w == 0) {
+        for (int bb = b; bb < p.B; bb += p.ngroups) {
+          int32_t* on = p.out_nodes + (size_t)bb * p.T_max;
+          int32_t* ot = p.out_tokens + (size_t)bb * p.T_max;
+          for (int i = tid; i < p.T_max; i += kAccThreads) { on[i] = -1; ot[i] = -1; }
+          if (tid == 0) {
+            p.out_count[bb] = 0;
+            if (p.out_passes) p.out_passes[bb] = 0;
+            if (bb == b || p.status[bb] == SV_TREE_OK) p.status[bb] = SV_TREE_E_SYNC;
+          }
+        }
+      }
       return;
     }
     if (nonfinite) st = SV_TREE_E_NONFINITE;
@@ -628,8 +685,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       }
       continue;
     }
-    // outputs: the emitted token by its owner, everything else by workgroup 0
-    if (w == owner && tid == 0) otoks[path_len] = emitted;
+    // outputs, all by workgroup 0
     if (w == 0) {
       for (int i = tid; i < p.T_max; i += kAccThreads) {
         if (i < path_len) {
@@ -637,7 +693,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
           otoks[i] = tok_s[path_s[i]];
         } else {
           onodes[i] = -1;
-          if (i != path_len) otoks[i] = -1;
+          otoks[i] = i == path_len ? emitted : -1;
         }
       }
       if (tid == 0) {
@@ -709,6 +765,11 @@ sv_status launch_accept(const sv_tree* t, int32_t* tree_status, const sv_accept_
   wp.ngroups = pl.ngroups;
   wp.bf16 = a->logit_dtype == SV_BF16;
   wp.sibling_mode = a->sibling_mode;
+  // one exchange wait may last 2 s (200M ticks of the 100 MHz counter);
+  // SV_WALK_WAIT_TICKS sets another bound, e.g. 0 to make every wait that
+  // does not find its value at once give up (a test of the give-up path)
+  wp.wait_ticks = 200000000ull;
+  if (const char* ov = getenv("SV_WALK_WAIT_TICKS")) wp.wait_ticks = strtoull(ov, nullptr, 10);
   // exchange words start at zero on every call (a fill kernel: no memset
   // node, so the call can be captured in a graph; a verify step's mask kernel
   // zeroes them instead)

@@ -72,7 +72,8 @@ enum {
   SV_TREE_E_TOKEN = 4,     /* a draft token tokens[b][i], 1 <= i < T_b, outside [0, V) */
   SV_TREE_E_NONFINITE = 5, /* a NaN or +-Inf in the logits row of a node the walk visits */
   SV_TREE_E_NOQ = 6,       /* temperature[b] > 0 but q_probs is NULL                  */
-  SV_TREE_E_SYNC = 7,      /* internal: a cross-workgroup wait timed out              */
+  SV_TREE_E_SYNC = 7,      /* a cross-workgroup wait of the walk timed out (see
+                              sv_spec_accept); outputs -1 / count 0                    */
   SV_TREE_E_CACHE = 8,     /* commit: L_b + out_count[b] exceeds L_max (or L_b < 0)   */
   SV_TREE_E_PATH = 9,      /* commit: out_count[b] > T_b or a path entry outside [1, T_b) */
   SV_TREE_E_PROB = 10      /* tree builder: a draft probability outside [0, 1] or NaN  */
@@ -178,8 +179,12 @@ sv_status sv_tree_attn(const sv_tree* tree, const uint64_t* anc, const int32_t* 
  *   ws / ws_bytes: at least sv_workspace_bytes(tree, NULL, a) bytes, 256-byte
  *   aligned.  The walk kernel's workgroups (at most one per CU) wait for one
  *   another, so all of them must be resident together: on a device shared with
- *   other work, workgroups queued behind it start when it ends; a wait longer
- *   than 2 s reports SV_TREE_E_SYNC.  Two walks that overlap on one device
+ *   other work, workgroups queued behind it start when it ends.  A wait longer
+ *   than 2 s gives up: the sequence being walked, and every later sequence the
+ *   same workgroup group would have walked, get SV_TREE_E_SYNC (a sequence
+ *   with its own data error keeps that status) and -1 / count 0 outputs, and
+ *   every workgroup ends.  Sequences finished before that keep their results.
+ *   (One workgroup of each group writes all of its sequences' outputs.)  Two walks that overlap on one device
  *   (calls on different streams) can each take part of the CUs the other's
  *   groups need, and then both end with SV_TREE_E_SYNC: order walks on one
  *   device (one stream, or events between streams).  Returns

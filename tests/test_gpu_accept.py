@@ -196,3 +196,54 @@ def test_accept_on_two_streams_ordered_by_events():
         got = dev.accept_results()
         for k in ("out_nodes", "out_tokens", "out_count", "out_passes"):
             np.testing.assert_array_equal(got[k], serial[i][k])
+
+
+def test_accept_gives_up_cleanly_when_waits_end_at_once():
+    """With the exchange-wait bound at 0 ticks (SV_WALK_WAIT_TICKS=0) every
+    wait that does not find its value at once gives up, as when a group's
+    workgroups are not all resident together.  Every workgroup still ends.
+    Each sequence is then either complete and equal to the oracle, or marked
+    SV_TREE_E_SYNC with -1 / count 0 outputs (a sequence with its own data
+    error keeps that status); once a group gives up at one of its sequences,
+    its later sequences are marked too.  A call with the normal bound on the
+    same buffers then gives the oracle's results."""
+    need_gpu()
+    import os
+    spec = _spec(cfg_id=224, B=64, V=131072, tree=("widths", [2, 2]), tau=1.0)
+    inst = make_instance(spec, 6, with_attn=False)
+    inst.parent[40, 2] = 2                        # a data error of its own (parent not before the node)
+    _, _, _, status = oracle.tree_mask(inst.parent, inst.num_nodes, inst.T_max)
+    ref = oracle.spec_accept(inst.parent, inst.num_nodes, inst.tokens, inst.target_logits, "bf16",
+                             inst.q_probs, inst.temperature, inst.u_accept, inst.u_sample, status)
+    dev = sv_problem(inst, with_attn=False)
+    say("accept give-up path: SV_WALK_WAIT_TICKS=0, B=64 V=131072 (2 sequences per group)")
+    os.environ["SV_WALK_WAIT_TICKS"] = "0"
+    try:
+        dev.mask_build()
+        dev.spec_accept()
+        res = dev.accept_results()
+    finally:
+        os.environ.pop("SV_WALK_WAIT_TICKS", None)
+    import torch
+    B = inst.B
+    ngroups = min(B, torch.cuda.get_device_properties(0).multi_processor_count // 8)   # 8 chunks of 16384
+    st = res["status"]
+    n_sync = int((st == oracle.TREE_E_SYNC).sum())
+    say(f"  gave up on {n_sync} of {B} sequences")
+    assert st[40] == oracle.TREE_E_PARENT
+    for b in range(B):
+        if st[b] == oracle.TREE_E_SYNC or b == 40:
+            assert res["out_count"][b] == 0, b
+            assert (res["out_nodes"][b] == -1).all() and (res["out_tokens"][b] == -1).all(), b
+            assert res["out_passes"][b] == 0, b
+            if st[b] == oracle.TREE_E_SYNC and b + ngroups < B and b + ngroups != 40:
+                assert st[b + ngroups] == oracle.TREE_E_SYNC, (b, st[b + ngroups])
+        else:
+            assert st[b] == oracle.TREE_OK, (b, st[b])
+            np.testing.assert_array_equal(res["out_nodes"][b], ref["out_nodes"][b])
+            np.testing.assert_array_equal(res["out_tokens"][b], ref["out_tokens"][b])
+            assert res["out_count"][b] == ref["out_count"][b]
+    say("  normal bound on the same buffers")
+    dev.mask_build()
+    dev.spec_accept()
+    check_accept(dev.accept_results(), ref, "after give-up")
