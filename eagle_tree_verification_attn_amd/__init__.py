@@ -89,6 +89,16 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m eagle_tree_verification_attn_amd.build`")
+        # torch ships its own HIP runtime under the same soname as the system
+        # one libsv.so is linked against.  Loaded first, torch's runtime
+        # satisfies libsv.so's dependency, so the process has one runtime and
+        # torch's streams and memory are valid in the library.  Loaded the
+        # other way round, the process would get two runtimes and torch would
+        # find no GPU.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
         L.sv_tree_mask_build.argtypes = [P(SvTree), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
