@@ -8,7 +8,7 @@ library fails loudly (build it with ``python -m eagle_tree_verification_attn_amd
 
 Entry points (same names as the C ABI):
     sv_tree_mask_build, sv_tree_attn, sv_spec_accept, sv_verify_step,
-    sv_commit_accepted, sv_workspace_bytes, sv_status_string, sv_last_error
+    sv_verify_step_noalloc, sv_commit_accepted, sv_workspace_bytes, sv_status_string, sv_last_error
 """
 import ctypes
 import os
@@ -24,7 +24,7 @@ SV_TREE_E_CACHE, SV_TREE_E_PATH, SV_TREE_E_PROB = 8, 9, 10
 SV_F32, SV_BF16 = 0, 1
 SV_SIB_WITHOUT_REPLACEMENT, SV_SIB_IID = 0, 1
 
-EXPORTS = ["sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step",
+EXPORTS = ["sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_verify_step_noalloc",
            "sv_commit_accepted", "sv_workspace_bytes", "sv_status_string", "sv_last_error",
            "sv_eagle2_state_bytes", "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish",
            "sv_draft_head"]
@@ -109,6 +109,8 @@ def lib():
         L.sv_verify_step.argtypes = [P(SvTree), P(SvAttnArgs), P(SvAcceptArgs), ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
+        L.sv_verify_step_noalloc.argtypes = [P(SvTree), P(SvAttnArgs), P(SvAcceptArgs), ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.sv_commit_accepted.argtypes = [P(SvTree), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          P(SvCommitArgs), ctypes.c_void_p]
         L.sv_eagle2_state_bytes.argtypes = [P(SvEagle2Cfg)]
@@ -127,7 +129,8 @@ def lib():
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_last_error.argtypes = []
         L.sv_last_error.restype = ctypes.c_char_p
-        for f in ("sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_commit_accepted",
+        for f in ("sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_verify_step_noalloc",
+                  "sv_commit_accepted",
                   "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish", "sv_draft_head"):
             getattr(L, f).restype = ctypes.c_int32
         _lib = L
@@ -232,6 +235,12 @@ def sv_verify_step(tree, attn, acc, anc, depth, tree_status, ws, stream=None, ra
     return _check(lib().sv_verify_step(ctypes.byref(tree), ctypes.byref(attn), ctypes.byref(acc), _ptr(anc),
                                        _ptr(depth), _ptr(tree_status), _ptr(ws), nbytes, _stream(stream)),
                   "sv_verify_step", raise_on_error)
+
+
+def sv_verify_step_noalloc(tree, attn, acc, anc, depth, tree_status, stream=None, raise_on_error=True):
+    return _check(lib().sv_verify_step_noalloc(ctypes.byref(tree), ctypes.byref(attn), ctypes.byref(acc), _ptr(anc),
+                                               _ptr(depth), _ptr(tree_status), _stream(stream)),
+                  "sv_verify_step_noalloc", raise_on_error)
 
 
 def sv_commit_accepted(tree, tree_status, out_nodes, out_count, commit, stream=None, raise_on_error=True):

@@ -155,6 +155,67 @@ sv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   return SV_OK;
 }
 
+// Mask -> attention -> accept on one stream.  ws_of(need) gives the workspace
+// for `need` bytes (or NULL after setting the error): the caller's buffer, or
+// the library's own scratch array.
+template <class WsOf>
+sv_status verify_step_impl(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc, uint64_t* anc,
+                           int32_t* depth, int32_t* tree_status, WsOf ws_of, void* stream) {
+  sv_status st = check_tree(tree, true);
+  if (st) return st;
+  if ((st = check_attn(tree, attn))) return st;
+  if ((st = check_accept(tree, acc))) return st;
+  if (tree->B > 0 && (!anc || !depth || !tree_status)) { set_error("anc/depth/tree_status is NULL"); return SV_E_NULL; }
+  AttnPlan ap;
+  AcceptPlan cp;
+  if (!plan_attention(tree, attn, &ap)) { set_error("no attention plan"); return SV_E_UNSUPPORTED; }
+  if (!plan_accept(tree, acc, &cp)) { set_error("no accept plan"); return SV_E_UNSUPPORTED; }
+  // the walk's exchange words follow the attention's partial results, so the
+  // mask kernel can zero them before attention runs
+  const size_t acc_base = align_up(ap.ws_bytes, kWsAlign);
+  cp.off_xchg += acc_base;
+  void* ws = nullptr;
+  if ((st = ws_of(acc_base + cp.ws_bytes, &ws))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t* xchg = tree->B > 0 ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + cp.off_xchg) : nullptr;
+  if ((st = launch_mask(tree, anc, depth, tree_status, xchg, tree->B > 0 ? accept_exchange_words(cp) : 0, s)))
+    return st;
+  if ((st = launch_attention(tree, anc, tree_status, attn, ap, ws, s))) return st;
+  return launch_accept(tree, tree_status, acc, cp, ws, false, s);
+}
+
+// The library's own scratch memory for sv_verify_step_noalloc: one array per
+// device, made when the library's code object is loaded on that device and
+// kept until the process ends.  Host code never passes `scratch` itself (on
+// the host that name only stands for the symbol): it asks the runtime for the
+// array's device address once per device and passes that.
+constexpr size_t kScratchBytes = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's scratch array (NULL after setting the
+// error when the runtime cannot give it).  Looked up once per device, with
+// that device current, by the first call on it.
+void* scratch_address() {
+  static void* addr[64];
+  static hipError_t err[64];
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    set_error("no current HIP device (or more than 64)");
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (!addr[dev]) {
+    set_error("scratch array of device %d: hipGetSymbolAddress failed: %s", dev, hipGetErrorString(err[dev]));
+    return nullptr;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 }  // namespace sv
 
@@ -201,26 +262,26 @@ sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv
                          uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws, size_t ws_bytes,
                          void* stream) {
   clear_error();
-  sv_status st = check_tree(tree, true);
-  if (st) return st;
-  if ((st = check_attn(tree, attn))) return st;
-  if ((st = check_accept(tree, acc))) return st;
-  if (tree->B > 0 && (!anc || !depth || !tree_status)) { set_error("anc/depth/tree_status is NULL"); return SV_E_NULL; }
-  AttnPlan ap;
-  AcceptPlan cp;
-  if (!plan_attention(tree, attn, &ap)) { set_error("no attention plan"); return SV_E_UNSUPPORTED; }
-  if (!plan_accept(tree, acc, &cp)) { set_error("no accept plan"); return SV_E_UNSUPPORTED; }
-  // the walk's exchange words follow the attention's partial results, so the
-  // mask kernel can zero them before attention runs
-  const size_t acc_base = align_up(ap.ws_bytes, kWsAlign);
-  cp.off_xchg += acc_base;
-  if ((st = check_ws(ws, ws_bytes, acc_base + cp.ws_bytes))) return st;
-  hipStream_t s = (hipStream_t)stream;
-  uint64_t* xchg = tree->B > 0 ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + cp.off_xchg) : nullptr;
-  if ((st = launch_mask(tree, anc, depth, tree_status, xchg, tree->B > 0 ? accept_exchange_words(cp) : 0, s)))
-    return st;
-  if ((st = launch_attention(tree, anc, tree_status, attn, ap, ws, s))) return st;
-  return launch_accept(tree, tree_status, acc, cp, ws, false, s);
+  auto caller_ws = [&](size_t need, void** out) {
+    *out = ws;
+    return check_ws(ws, ws_bytes, need);
+  };
+  return verify_step_impl(tree, attn, acc, anc, depth, tree_status, caller_ws, stream);
+}
+
+sv_status sv_verify_step_noalloc(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
+                                 uint64_t* anc, int32_t* depth, int32_t* tree_status, void* stream) {
+  clear_error();
+  auto own_ws = [&](size_t need, void** out) -> sv_status {
+    if (need > kScratchBytes) {
+      set_error("sv_verify_step_noalloc: this problem needs %zu bytes of scratch, more than the %zu the library "
+                "holds; call sv_verify_step with a workspace of sv_workspace_bytes bytes", need, kScratchBytes);
+      return SV_E_WORKSPACE;
+    }
+    *out = need > 0 ? scratch_address() : nullptr;
+    return (need > 0 && !*out) ? SV_E_HIP : SV_OK;
+  };
+  return verify_step_impl(tree, attn, acc, anc, depth, tree_status, own_ws, stream);
 }
 
 sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const int32_t* out_nodes,

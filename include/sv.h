@@ -203,6 +203,24 @@ sv_status sv_verify_step(const sv_tree* tree, const sv_attn_args* attn, const sv
                          uint64_t* anc, int32_t* depth, int32_t* tree_status, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* sv_verify_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The step's scratch memory (the
+ * attention's partial results and the walk's exchange words, the same layout
+ * sv_verify_step puts in its workspace) lives in one array per device inside
+ * the library, 64 MiB (67108864 bytes), made when the library's code is
+ * loaded on that device and kept until the process ends.  The first call on
+ * a device looks up that device's array address once.  The call allocates
+ * and frees nothing, and the mask kernel zeroes what must start at zero, so
+ * results equal those of sv_verify_step.  Every call on one device shares
+ * that device's array: calls that overlap on one device (different streams,
+ * or host threads without ordering) race on it and must be ordered by the
+ * caller.  Returns SV_E_WORKSPACE, before launching anything, when the
+ * problem needs more than 64 MiB (sv_workspace_bytes(tree, attn, acc) >
+ * 67108864); other errors as sv_verify_step. */
+sv_status sv_verify_step_noalloc(const sv_tree* tree, const sv_attn_args* attn, const sv_accept_args* acc,
+                                 uint64_t* anc, int32_t* depth, int32_t* tree_status, void* stream);
+
 /* Commit of the accepted path: cache growth and drafter features. */
 typedef struct {
   int32_t Hkv, D;           /* KV heads and head dim of the caches (any D with D*size % 16 == 0) */
