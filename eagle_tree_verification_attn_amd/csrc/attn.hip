@@ -257,21 +257,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   }
 
-  // acc: O^T tiles; lsum: the row sums of P, accumulated by an MFMA with an
-  // all-ones A operand, so every element of lsum[qt] holds its column's sum.
+  // acc: O^T tiles; lsum: the row sums of P.  Each block's row sums come
+  // from an MFMA with an all-ones A operand (every element of its result
+  // holds the column's sum), which also serves as the overflow test below.
   // mu: the running offset of the lane's row in raw dot-product units,
   // subtracted by the score MFMA itself (its accumulator starts at
   // cinit = -mu); valid once a visible key has set it.  With c = scale *
   // log2(e), P = 2^(c (dot - mu)) with c (dot - mu) <= 8 kept.
-  f32x4 acc[NT][DT], lsum[NT], cinit[NT];
-  float mu[NT];
+  f32x4 acc[NT][DT], cinit[NT];
+  float mu[NT], lsum[NT];
   bool valid[NT];
 #pragma unroll
   for (int qt = 0; qt < NT; ++qt) {
     mu[qt] = 0.f;
     valid[qt] = false;
     cinit[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lsum[qt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -399,44 +400,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
 
   // ---- online softmax of s, P packed to bf16 for the PV MFMA and kept in the
-  // registers of s[qt][0] (so only s lives from one phase to the next).  The
-  // scores already are dot - mu (raw units).  Each lane compares the maximum
-  // of its values with the bound 8 / c; only when some lane exceeds it, or a
-  // row has no offset yet, does the wave form column maxima and raise offsets.
+  // registers of s[qt][1] (so only s lives from one phase to the next).  The
+  // scores already are dot - mu (raw units).  While some row of the wave has
+  // no offset yet, the wave forms column maxima and sets (or raises) offsets
+  // first.  Otherwise P = 2^(c s) is formed at once and checked through the
+  // block's row sums, which the ones-MFMA yields anyway: a row sum above
+  // 2^64 (or not finite) means some score exceeded the row's offset by more
+  // than 64 / c, and only then is the block scored again and the offsets
+  // raised past the block's maximum.  Between raises P stays below 2^64, so
+  // fp32 sums of at most 2^31 weights cannot overflow.
   const float c2 = p.scale_log2, thr = p.raise_raw;
-  auto softmax = [&]() {
-    float pmax = -INFINITY;
-    bool unset = false;
+  bool all_valid = false;   // wave-uniform: every row of the wave has an offset
+  auto raise_offsets = [&]() {
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
-      pmax = fmaxf(pmax, fmaxf(fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3])),
-                               fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]))));
-      unset |= !valid[qt];
-    }
-    if (__any(pmax > thr || unset)) {
+      const float a0 = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
+      const float a1 = fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]));
+      const float cm = col_max4(fmaxf(a0, a1));   // column max of dot - mu
+      // a row without an offset takes the first visible maximum (its
+      // accumulators are still zero); a row with one raises it past 8 / c
+      const bool raise = valid[qt] ? cm > thr : cm > -INFINITY;
+      if (raise) {
+        if (valid[qt]) {
+          const float alpha = __builtin_amdgcn_exp2f(-cm * c2);
 #pragma unroll
-      for (int qt = 0; qt < NT; ++qt) {
-        const float a0 = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
-        const float a1 = fmaxf(fmaxf(s[qt][1][0], s[qt][1][1]), fmaxf(s[qt][1][2], s[qt][1][3]));
-        const float cm = col_max4(fmaxf(a0, a1));   // column max of dot - mu
-        // a row without an offset takes the first visible maximum (its
-        // accumulators are still zero); a row with one raises it past 8 / c
-        const bool raise = valid[qt] ? cm > thr : cm > -INFINITY;
-        if (raise) {
-          if (valid[qt]) {
-            const float alpha = __builtin_amdgcn_exp2f(-cm * c2);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
-            lsum[qt] *= alpha;
-          }
-          mu[qt] += cm;
-          valid[qt] = true;
-          cinit[qt] = f32x4{-mu[qt], -mu[qt], -mu[qt], -mu[qt]};
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) s[qt][kt] -= cm;
+          for (int dt = 0; dt < DT; ++dt) acc[qt][dt] *= alpha;
+          lsum[qt] *= alpha;
         }
+        mu[qt] += cm;
+        valid[qt] = true;
+        cinit[qt] = f32x4{-mu[qt], -mu[qt], -mu[qt], -mu[qt]};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) s[qt][kt] -= cm;
       }
     }
+    bool v = true;
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) v = v && valid[qt];
+    all_valid = __all(v);
+  };
+  f32x4 blk[NT];   // the block's row sums of P
+  auto exps = [&]() {
 #pragma unroll
     for (int qt = 0; qt < NT; ++qt) {
       float pv[8];
@@ -447,8 +451,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
-      s[qt][0] = __builtin_bit_cast(f32x4, make_uint4(w[0], w[1], w[2], w[3]));
+      s[qt][1] = __builtin_bit_cast(f32x4, make_uint4(w[0], w[1], w[2], w[3]));
     }
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt)
+      blk[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, s[qt][1]),
+                                                        f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  };
+  auto softmax = [&](int n) {
+    if (!all_valid) raise_offsets();
+    exps();
+    bool ok = true;
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) ok = ok && blk[qt][0] <= 0x1p64f;
+    if (!__all(ok)) {
+      // a score ran more than 64 / c past its row's offset: score the block
+      // again (its K tile is still in LDS), raise the offsets, redo P
+      scores(n);
+      raise_offsets();
+      exps();
+    }
+#pragma unroll
+    for (int qt = 0; qt < NT; ++qt) lsum[qt] += blk[qt][0];
   };
 
   // ---- O^T += V^T P^T for key block n.  Lane (g, c) needs V[key][16 dt + c]
@@ -458,10 +482,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const __bf16* vs = smem + (n % kStages) * STAGE + TILE;
     bf16x8 pk[NT];
 #pragma unroll
-    for (int qt = 0; qt < NT; ++qt) pk[qt] = __builtin_bit_cast(bf16x8, s[qt][0]);
-#pragma unroll
-    for (int qt = 0; qt < NT; ++qt)
-      lsum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[qt], lsum[qt], 0, 0, 0);
+    for (int qt = 0; qt < NT; ++qt) pk[qt] = __builtin_bit_cast(bf16x8, s[qt][1]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const bf16x4 lo = lds_read_tr16(vs + voff[dt]);
@@ -483,7 +504,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // copies and keeps the barriers, leaving its SIMD to the other waves
     if (wave_active) {
       scores(it);
-      softmax();
+      softmax(it);
       pv_product(it);
     }
   }
@@ -491,7 +512,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // ---- epilogue
 #pragma unroll
   for (int qt = 0; qt < NT; ++qt) {
-    const float l = lsum[qt][0];
+    const float l = lsum[qt];
     const int r = rrow[qt];
     if (r >= p.T_max * G) continue;
     const int t = r / G, h = kvh * G + r % G;
