@@ -127,19 +127,17 @@ __device__ inline void load_raw(const void* rowp, int c0, int c1, u32x4 (&raw)[k
   }
 }
 
-// Statistics of this workgroup's chunk of one logits row:
+// Statistics of this workgroup's chunk of one logits row, from its words
+// already loaded by load_raw:
 //   stochastic rows: (m_c, s_c) = (chunk max, sum of e(v) = 2^((z(v) - m_c) k)),
 //                    and e(v) stored in LDS at ec[v - c0];
 //   greedy rows:     (m_c, i_c) = (chunk max, its lowest index);
 //   flag: a NaN or an infinity anywhere in the chunk.
 // The result is returned to thread 0 as (m, s or index bits, flag, 0).
-template <bool BF16, bool VEC>
-__device__ float4 chunk_stats(const void* rowp, int c0, int c1, bool greedy, float k, float* ec,
+template <bool BF16, bool VEC, int RH = BF16 ? 1 : 2>
+__device__ float4 chunk_stats(const u32x4 (&raw)[kBatch][RH], int c0, int c1, bool greedy, float k, float* ec,
                               float* red_m, float* red_s, int* red_i, int* red_f) {
-  constexpr int RH = BF16 ? 1 : 2;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  u32x4 raw[kBatch][RH];
-  load_raw<BF16, VEC>(rowp, c0, c1, raw);
   // Non-finite test on the raw words: an all-ones exponent field plus one
   // carries into the field's top bit.  Clamped loads repeat real entries of
   // this chunk, so they change neither this flag nor the maximum.
@@ -196,7 +194,7 @@ __device__ float4 chunk_stats(const void* rowp, int c0, int c1, bool greedy, flo
 #pragma unroll
   for (int q = 0; q < kBatch; ++q)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, elem8<BF16, RH>(raw[q], e));
+    for (int e = 0; e < 8; e += 2) m = fmaxf(m, fmaxf(elem8<BF16, RH>(raw[q], e), elem8<BF16, RH>(raw[q], e + 1)));
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   __syncthreads();   // the previous user of red_* is done
   if (lane == 0) { red_m[wv] = m; red_f[wv] = any_bad; }
@@ -211,19 +209,22 @@ __device__ float4 chunk_stats(const void* rowp, int c0, int c1, bool greedy, flo
     const int i = c0 + (tid + q * kAccThreads) * 8;
     float ev[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ev[e] = __builtin_amdgcn_exp2f(fmaf(elem8<BF16, RH>(raw[q], e), k, -mk));
-      s += (i + e < c1) ? ev[e] : 0.f;
-    }
+    for (int e = 0; e < 8; ++e) ev[e] = __builtin_amdgcn_exp2f(fmaf(elem8<BF16, RH>(raw[q], e), k, -mk));
     if (VEC) {
-      // a clamped group holds entries [c0, c0 + 8) and rewrites them unchanged
+      // chunk ends are multiples of 8: a group of 8 is in the chunk or is a
+      // clamped repeat of entries [c0, c0 + 8), which rewrites them unchanged
+      const float gs = ((ev[0] + ev[1]) + (ev[2] + ev[3])) + ((ev[4] + ev[5]) + (ev[6] + ev[7]));
+      s += i < c1 ? gs : 0.f;
       const int ic = i < c1 ? i : c0;
       *reinterpret_cast<f32x4*>(ec + (ic - c0)) = f32x4{ev[0], ev[1], ev[2], ev[3]};
       *reinterpret_cast<f32x4*>(ec + (ic - c0) + 4) = f32x4{ev[4], ev[5], ev[6], ev[7]};
     } else if (i < c1) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (i + e < c1) ec[i - c0 + e] = ev[e];
+        if (i + e < c1) {
+          s += ev[e];
+          ec[i - c0 + e] = ev[e];
+        }
     }
   }
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -395,26 +396,51 @@ struct GroupXchg {
 // node's row (one exchange); each rejection then needs the mass of the new
 // residual over the vocabulary (one exchange each).  Only the rows of visited
 // nodes are read.
+// Children of the node being expanded, in increasing position: bit c of
+// cm[n] is set iff parent[c] == n (positions below 256, words of 64).
+// Returns the smallest child of n after position `after`, or -1.
+__device__ inline int next_child(const uint64_t (*cm)[kMaxT / 64], int n, int after, int W) {
+  int wd = (after + 1) >> 6;
+  if (wd >= W) return -1;
+  uint64_t m = cm[n][wd] & (~0ull << ((after + 1) & 63));
+  while (true) {
+    if (m) return wd * 64 + __ffsll((unsigned long long)m) - 1;
+    if (++wd >= W) return -1;
+    m = cm[n][wd];
+  }
+}
+
+// Wave-wide sum and maximum (every lane gets the result).
+__device__ inline float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
+  constexpr int RH = BF16 ? 1 : 2;
   // Per-sequence data gathered once into LDS, so the walk's scalar decisions
   // read LDS instead of chaining dependent global loads.
-  __shared__ int par_s[kMaxT];
   __shared__ int tok_s[kMaxT];
   __shared__ int path_s[kMaxT];
   __shared__ float zx_s[kMaxT];   // logit of node c's token in its parent's row
   __shared__ float qx_s[kMaxT];   // q of node c's token in its parent's row
   __shared__ float ua_s[kMaxT];
   __shared__ float us_s[kMaxT];
+  __shared__ uint64_t cm_s[kMaxT][kMaxT / 64];   // children of every node, as bit rows
   __shared__ float red[kAccThreads / 64];
   __shared__ float red_m[kAccThreads / 64], red_s[kAccThreads / 64];
   __shared__ int red_i[kAccThreads / 64], red_f[kAccThreads / 64];
   __shared__ float masses[64];
   __shared__ float xv[64 * kXWords];   // the group's exchanged values
   __shared__ float pubv[kXWords];
-  __shared__ float bcast, m_b, ls_b, f_b;
+  __shared__ float bcast, m_b, ls_b, f_b, excl_b;
   __shared__ uint32_t tok_b;
-  __shared__ int ibcast, am_b, bad_b;
+  __shared__ int ibcast, ybcast, am_b, bad_b;
   __shared__ int flags_s;
 
   const int tid = threadIdx.x;
@@ -429,40 +455,57 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
   float* pc = cache_s;
   float* qc = cache_s + p.chunk;
   const int len = c1 - c0;
+  auto logits_row = [&](size_t row) {
+    return BF16 ? (const void*)(reinterpret_cast<const uint16_t*>(p.logits) + row * p.V)
+                : (const void*)(reinterpret_cast<const float*>(p.logits) + row * p.V);
+  };
 
   for (int b = grp; b < p.B; b += p.ngroups) {
+    const size_t rowbase = (size_t)b * p.T_max;
+    // The root's row is read by every valid sequence: its chunk loads go out
+    // first, and the tree is gathered while they are in flight.  (Row 0 of
+    // every sequence lies inside the logits tensor, so the loads are in
+    // bounds whatever the sequence's status.)
+    u32x4 raw[kBatch][RH];
+    load_raw<BF16, VEC>(logits_row(rowbase), c0, c1, raw);
     int st = p.status[b];
     const int Tb = p.num_nodes[b];
     if (st == SV_TREE_OK && (Tb < 1 || Tb > p.T_max)) st = SV_TREE_E_COUNT;
+    const int W = (Tb + 63) >> 6;
     const float tau = p.temperature[b];
     const bool greedy = greedy_temp(tau);
     const float k = greedy ? 0.f : kLog2e / tau;
     int32_t* onodes = p.out_nodes + (size_t)b * p.T_max;
     int32_t* otoks = p.out_tokens + (size_t)b * p.T_max;
-    const size_t rowbase = (size_t)b * p.T_max;
     __syncthreads();
     if (tid == 0) flags_s = 0;
+    if (st == SV_TREE_OK)
+      for (int i = tid; i < Tb * (kMaxT / 64); i += kAccThreads) cm_s[i / (kMaxT / 64)][i % (kMaxT / 64)] = 0ull;
     __syncthreads();
     if (st == SV_TREE_OK) {
-      // round 1: tree, tokens, uniforms
+      // round 1: tree (as child bit rows), tokens, uniforms.  A valid tree
+      // has 0 <= parent[c] < c for 1 <= c < T_b.
       for (int i = tid; i < Tb; i += kAccThreads) {
-        par_s[i] = p.parent[rowbase + i];
         const int x = p.tokens[rowbase + i];
         tok_s[i] = x;
         ua_s[i] = p.u_accept[rowbase + i];
         us_s[i] = p.u_sample[rowbase + i];
-        if (i > 0 && (x < 0 || x >= p.V)) atomicOr(&flags_s, 1);   // the root's token is not read
+        if (i > 0) {
+          const int par = p.parent[rowbase + i];
+          if (par >= 0 && par < i) atomicOr(reinterpret_cast<unsigned long long*>(&cm_s[par][i >> 6]), 1ull << (i & 63));
+          else atomicOr(&flags_s, 2);   // only a caller's own status could let such a tree through
+          if (x < 0 || x >= p.V) atomicOr(&flags_s, 1);   // the root's token is not read
+        }
       }
       __syncthreads();
-      if (flags_s & 1) st = SV_TREE_E_TOKEN;
+      if (flags_s & 2) st = SV_TREE_E_PARENT;
+      else if (flags_s & 1) st = SV_TREE_E_TOKEN;
       else if (!greedy && p.q_probs == nullptr) st = SV_TREE_E_NOQ;
       // round 2: each candidate's logit and draft probability in its parent's row
       if (st == SV_TREE_OK && !greedy) {
         for (int c = 1 + tid; c < Tb; c += kAccThreads) {
-          const int n = par_s[c], x = tok_s[c];
-          zx_s[c] = load_logit(BF16 ? (const void*)(reinterpret_cast<const uint16_t*>(p.logits) + (rowbase + n) * p.V)
-                                    : (const void*)(reinterpret_cast<const float*>(p.logits) + (rowbase + n) * p.V),
-                               (size_t)x, BF16);
+          const int n = p.parent[rowbase + c], x = tok_s[c];
+          zx_s[c] = load_logit(logits_row(rowbase + n), (size_t)x, BF16);
           qx_s[c] = p.q_probs[(rowbase + n) * p.V + x];
         }
       }
@@ -472,34 +515,38 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
     int n = 0, path_len = 0, passes = 0, emitted = -1, owner = -1;
     bool sync_ok = true, nonfinite = false;
     while (st == SV_TREE_OK) {
-      const void* zrow = BF16 ? (const void*)(reinterpret_cast<const uint16_t*>(p.logits) + (rowbase + n) * p.V)
-                              : (const void*)(reinterpret_cast<const float*>(p.logits) + (rowbase + n) * p.V);
       const float* qrow = greedy ? nullptr : p.q_probs + (rowbase + n) * p.V;
-      // ---- statistics of node n's row: every chunk, one exchange
+      // ---- statistics of node n's row: every chunk, one exchange (the
+      // root's chunk was loaded at the start)
+      if (n != 0) load_raw<BF16, VEC>(logits_row(rowbase + n), c0, c1, raw);
       {
-        const float4 loc = chunk_stats<BF16, VEC>(zrow, c0, c1, greedy, k, pc, red_m, red_s, red_i, red_f);
+        const float4 loc = chunk_stats<BF16, VEC>(raw, c0, c1, greedy, k, pc, red_m, red_s, red_i, red_f);
         if (tid == 0) { pubv[0] = loc.x; pubv[1] = loc.y; pubv[2] = loc.z; }
         if (!gx.exchange(w, pubv, 3, xv)) { sync_ok = false; break; }
-        if (tid == 0) {
-          float M = -INFINITY, S = 0.f;
-          int I = 0, F = 0;
-          for (int cc = 0; cc < p.nchunk; ++cc) {
-            const float mc = xv[3 * cc], yc = xv[3 * cc + 1];
-            F |= __float_as_int(xv[3 * cc + 2]);
-            if (mc > M) { M = mc; I = __float_as_int(yc); }   // first chunk with the max: lowest index
-          }
+        // combined over the chunks by the first wave, one lane per chunk
+        if (tid < 64) {
+          const bool live = tid < p.nchunk;
+          const float mc = live ? xv[3 * tid] : -INFINITY;
+          const float yc = live ? xv[3 * tid + 1] : 0.f;
+          const float M = wave_max(mc);
+          // greedy: the first chunk holding the maximum has the lowest index
+          const uint64_t at_max = __ballot(live && mc == M);
+          const int first = at_max ? (int)__ffsll((unsigned long long)at_max) - 1 : 0;
+          const int I = __shfl(__float_as_int(yc), first);
+          const bool F = __any(live && __float_as_int(xv[3 * tid + 2]) != 0);
           if (!greedy) {
-            for (int cc = 0; cc < p.nchunk; ++cc) S += xv[3 * cc + 1] * __builtin_amdgcn_exp2f((xv[3 * cc] - M) * k);
+            const float S = wave_sum(live ? yc * __builtin_amdgcn_exp2f((mc - M) * k) : 0.f);
             const float ls = __log2f(S);
-            for (int cc = 0; cc < p.nchunk; ++cc)
-              masses[cc] = xv[3 * cc + 1] * __builtin_amdgcn_exp2f((xv[3 * cc] - M) * k - ls);
-            ls_b = ls;
-            // p(v) = e(v) f on this chunk
-            f_b = __builtin_amdgcn_exp2f((xv[3 * w] - M) * k - ls);
+            if (live) masses[tid] = yc * __builtin_amdgcn_exp2f((mc - M) * k - ls);
+            // p(v) = e(v) f on this workgroup's chunk
+            if (tid == w) f_b = __builtin_amdgcn_exp2f((mc - M) * k - ls);
+            if (tid == 0) ls_b = ls;
           }
-          m_b = M;
-          am_b = I;
-          bad_b = F;
+          if (tid == 0) {
+            m_b = M;
+            am_b = I;
+            bad_b = F;
+          }
         }
         __syncthreads();
       }
@@ -507,8 +554,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       int acc = -1;
       if (greedy) {
         const int am = am_b;
-        for (int i = n + 1; i < Tb; ++i)
-          if (par_s[i] == n && tok_s[i] == am) { acc = i; break; }
+        for (int c = next_child(cm_s, n, n, W); c >= 0; c = next_child(cm_s, n, c, W))
+          if (tok_s[c] == am) { acc = c; break; }
         if (acc >= 0) {
           if (tid == 0) path_s[path_len] = acc;
           ++path_len;
@@ -522,8 +569,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       const float m = m_b, ls = ls_b, f = f_b;
       float A = 0.f, Wn = 1.f, rm = 0.f, Adraw = 0.f;
       bool have_q = false;
-      for (int c = n + 1; c < Tb; ++c) {
-        if (par_s[c] != n) continue;
+      const int first_child = next_child(cm_s, n, n, W);
+      for (int c = first_child; c >= 0; c = next_child(cm_s, n, c, W)) {
         const float qx = qx_s[c];
         const float px = __builtin_amdgcn_exp2f(fmaf(zx_s[c] - m, k, -ls));
         const float Px = fmaxf(px - A * qx, 0.f) / Wn;
@@ -541,26 +588,30 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
           __syncthreads();
           have_q = true;
         }
-        float part = 0.f;
-        for (int i = tid * 4; i < len; i += kAccThreads * 4) {
+        // thread t sums entries 4t + 1024 j, j = 0..15, in four chains
+        float pa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kMaxChunk / (4 * kAccThreads); ++j) {
+          const int i = tid * 4 + j * 4 * kAccThreads;
           if (i + 4 <= len) {
             const float4 pp = *reinterpret_cast<const float4*>(pc + i);
             const float4 qq = *reinterpret_cast<const float4*>(qc + i);
-            part += fmaxf(fmaf(-An, qq.x, pp.x * f), 0.f) + fmaxf(fmaf(-An, qq.y, pp.y * f), 0.f) +
-                    fmaxf(fmaf(-An, qq.z, pp.z * f), 0.f) + fmaxf(fmaf(-An, qq.w, pp.w * f), 0.f);
-          } else {
-            for (int e = i; e < len; ++e) part += fmaxf(fmaf(-An, qc[e], pc[e] * f), 0.f);
+            pa[j & 3] += (fmaxf(fmaf(-An, qq.x, pp.x * f), 0.f) + fmaxf(fmaf(-An, qq.y, pp.y * f), 0.f)) +
+                         (fmaxf(fmaf(-An, qq.z, pp.z * f), 0.f) + fmaxf(fmaf(-An, qq.w, pp.w * f), 0.f));
+          } else if (i < len) {
+            for (int e = i; e < len; ++e) pa[j & 3] += fmaxf(fmaf(-An, qc[e], pc[e] * f), 0.f);
           }
         }
+        float part = (pa[0] + pa[1]) + (pa[2] + pa[3]);
         part = block_sum(part, red);
         if (tid == 0) pubv[0] = part;
         if (!gx.exchange(w, pubv, 1, xv)) { sync_ok = false; break; }
-        if (tid == 0) {
-          float tot = 0.f;
-          for (int cc = 0; cc < p.nchunk; ++cc) tot += xv[cc];
-          bcast = tot;
-          if (tot > 0.f)
-            for (int cc = 0; cc < p.nchunk; ++cc) masses[cc] = xv[cc];
+        if (tid < 64) {
+          const bool live = tid < p.nchunk;
+          const float v = live ? xv[tid] : 0.f;
+          const float tot = wave_sum(v);
+          if (tid == 0) bcast = tot;
+          if (tot > 0.f && live) masses[tid] = v;
         }
         __syncthreads();
         const float Wsum = bcast;
@@ -580,11 +631,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
         continue;
       }
       // draw at node n from P proportional to max(0, p - Adraw q) with u_sample[n]
-      bool leaf = true;
-      for (int c = n + 1; c < Tb; ++c)
-        if (par_s[c] == n) { leaf = false; break; }
-      if (leaf) ++passes;
-      __syncthreads();
+      if (first_child < 0) ++passes;   // a leaf: the bonus draw reads the row once more
       float total = 0.f;
       for (int cc = 0; cc < p.nchunk; ++cc) total += masses[cc];
       const float target = us_s[n] * total;
@@ -603,37 +650,65 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       if (w == owner) {
         // residual entry i of the chunk (q is only needed after a rejection)
         auto resid = [&](int i) { return have_q ? fmaxf(fmaf(-Adraw, qc[i], pc[i] * f), 0.f) : pc[i] * f; };
-        // scan the chunk in vocabulary order: thread t owns the contiguous
-        // segment [t * seg, (t + 1) * seg)
-        const int seg = (len + kAccThreads - 1) / kAccThreads;
-        const int s0 = min(tid * seg, len), s1 = min(s0 + seg, len);
+        // thread t owns the 64 entries [64 t, 64 t + 64) of the chunk
+        const int s0 = tid * 64;
         int y = -1;
         if (!fallback) {
-          float vs = 0.f;
-          for (int i = s0; i < s1; ++i) vs += resid(i);
+          float va[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int i = s0 + 4 * j;
+            if (i + 4 <= len) {
+              const float4 pp = *reinterpret_cast<const float4*>(pc + i);
+              if (have_q) {
+                const float4 qq = *reinterpret_cast<const float4*>(qc + i);
+                va[j & 3] += (fmaxf(fmaf(-Adraw, qq.x, pp.x * f), 0.f) + fmaxf(fmaf(-Adraw, qq.y, pp.y * f), 0.f)) +
+                             (fmaxf(fmaf(-Adraw, qq.z, pp.z * f), 0.f) + fmaxf(fmaf(-Adraw, qq.w, pp.w * f), 0.f));
+              } else {
+                va[j & 3] += (pp.x * f + pp.y * f) + (pp.z * f + pp.w * f);
+              }
+            } else {
+              for (int e = i; e < min(i + 4, len); ++e) va[j & 3] += resid(e);
+            }
+          }
+          const float vs = (va[0] + va[1]) + (va[2] + va[3]);
           float incl, excl, tot;
           block_scan(vs, red, &incl, &excl, &tot);
           if (tid == 0) ibcast = 0x7FFFFFFF;
           __syncthreads();
+          // the segment whose range of the cumulative mass holds the target
           if (cum + excl <= target && cum + incl > target) {
-            float run = cum + excl;
-            int found = -1, lastin = -1;
-            for (int i = s0; i < s1; ++i) {
-              const float v = resid(i);
-              if (v > 0.f) lastin = i;
-              run += v;
-              if (run > target) { found = i; break; }
-            }
-            if (found < 0) found = lastin;
-            if (found >= 0) atomicMin(&ibcast, c0 + found);
+            atomicMin(&ibcast, tid);
+            excl_b = excl;   // a single segment holds it (zero-mass segments are empty ranges)
           }
           __syncthreads();
-          if (ibcast != 0x7FFFFFFF) y = ibcast;
+          const int ts = ibcast;
+          if (ts != 0x7FFFFFFF && tid < 64) {
+            // the first wave scans that segment, one entry per lane
+            const int i = ts * 64 + tid;
+            const float v = i < len ? resid(i) : 0.f;
+            float x = v;
+            for (int off = 1; off < 64; off <<= 1) {
+              const float u = __shfl_up(x, off);
+              if (tid >= off) x += u;
+            }
+            const float base = cum + excl_b;
+            const uint64_t over = __ballot(base + x > target);
+            const uint64_t pos = __ballot(v > 0.f);
+            int hit = -1;
+            if (over) hit = (int)__ffsll((unsigned long long)over) - 1;
+            else if (pos) hit = 63 - __clzll((long long)pos);   // rounding left no crossing: the last entry with mass
+            if (tid == 0) ybcast = hit >= 0 ? c0 + ts * 64 + hit : -1;
+          } else if (ts == 0x7FFFFFFF && tid == 0) {
+            ybcast = -1;
+          }
+          __syncthreads();
+          y = ybcast;
         }
         if (y < 0) {
-          // rounding left no crossing: the largest entry of the chunk with positive mass
+          // no crossing at all: the largest entry of the chunk with positive mass
           int lp = -1;
-          for (int i = s0; i < s1; ++i)
+          for (int i = s0; i < min(s0 + 64, len); ++i)
             if (resid(i) > 0.f) lp = c0 + i;
           __syncthreads();
           if (tid == 0) ibcast = -1;
