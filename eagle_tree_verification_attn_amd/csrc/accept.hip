@@ -94,6 +94,82 @@ __device__ inline float elem8(const u32x4 (&w)[H], int e) {
   return __uint_as_float(w[e >> 2][e & 3]);
 }
 
+// ----------------------------------------------------------------------------
+// wave-wide reductions and scans on DPP lane moves and the gfx950 row swaps
+// (no LDS round trips); every lane of the wave must be active
+// ----------------------------------------------------------------------------
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+// the two values of a lane's row pair (rows 0/1, 2/3), then of its half pair
+__device__ inline void swap16(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ inline void swap32(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+// Butterflies within each row of 16 (quad_perm [1,0,3,2], [2,3,0,1], the
+// half-row mirror, the row mirror), then across rows: every lane gets the
+// wave's total.
+__device__ inline float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  uint32_t a, b;
+  swap16(__float_as_uint(v), a, b);
+  v = __uint_as_float(a) + __uint_as_float(b);
+  swap32(__float_as_uint(v), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  uint32_t a, b;
+  swap16(__float_as_uint(v), a, b);
+  v = fmaxf(__uint_as_float(a), __uint_as_float(b));
+  swap32(__float_as_uint(v), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ inline int wave_min_i(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x141>(v));
+  v = min(v, dpp_i<0x140>(v));
+  uint32_t a, b;
+  swap16((uint32_t)v, a, b);
+  v = min((int)a, (int)b);
+  swap32((uint32_t)v, a, b);
+  return min((int)a, (int)b);
+}
+// Inclusive prefix sum over the wave in lane order: within rows of 16 by
+// shifted adds (row_shr 1, 2, 4, 8; lanes shifted in from outside the row
+// add 0), then each row adds the totals of the rows before it.
+__device__ inline float wave_incl_scan(float x) {
+  const int lane = threadIdx.x & 63;
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+  const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  const int row = lane >> 4;
+  const float before = row == 0 ? 0.f : (row == 1 ? t0 : (row == 2 ? t0 + t1 : (t0 + t1) + t2));
+  return before + x;
+}
+
 // Raw 16-byte words of the logits: one per group of 8 (bf16) or two (fp32).
 // Without VEC (row not 16-byte aligned or V % 8 != 0) entries are read one by
 // one, entries past the chunk end again clamped.
@@ -169,10 +245,10 @@ __device__ float4 chunk_stats(const u32x4 (&raw)[kBatch][RH], int c0, int c1, bo
         if (i + e < c1 && x > m) { m = x; am = i + e; }   // strict: lowest index per thread
       }
     }
-    for (int off = 32; off > 0; off >>= 1) {
-      const float om = __shfl_xor(m, off);
-      const int oi = __shfl_xor(am, off);
-      if (om > m || (om == m && oi < am)) { m = om; am = oi; }
+    {
+      const float M = wave_max(m);
+      am = wave_min_i(m == M ? am : 0x7FFFFFFF);   // the lowest index holding the maximum
+      m = M;
     }
     __syncthreads();   // the previous user of red_* is done
     if (lane == 0) { red_m[wv] = m; red_i[wv] = am; red_f[wv] = any_bad; }
@@ -195,7 +271,7 @@ __device__ float4 chunk_stats(const u32x4 (&raw)[kBatch][RH], int c0, int c1, bo
   for (int q = 0; q < kBatch; ++q)
 #pragma unroll
     for (int e = 0; e < 8; e += 2) m = fmaxf(m, fmaxf(elem8<BF16, RH>(raw[q], e), elem8<BF16, RH>(raw[q], e + 1)));
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  m = wave_max(m);
   __syncthreads();   // the previous user of red_* is done
   if (lane == 0) { red_m[wv] = m; red_f[wv] = any_bad; }
   __syncthreads();
@@ -227,7 +303,7 @@ __device__ float4 chunk_stats(const u32x4 (&raw)[kBatch][RH], int c0, int c1, bo
         }
     }
   }
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  s = wave_sum(s);
   if (lane == 0) red_s[wv] = s;
   __syncthreads();
   if (tid == 0) {
@@ -274,7 +350,7 @@ __global__ void k_accept_clear(uint64_t* words, int n) {
 // k_accept_walk
 // ----------------------------------------------------------------------------
 __device__ inline float block_sum(float v, float* red) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  v = wave_sum(v);
   const int tid = threadIdx.x;
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = v;
@@ -290,12 +366,8 @@ __device__ inline float block_sum(float v, float* red) {
 // inclusive value of thread t-1) and the workgroup total.
 __device__ inline void block_scan(float v, float* red, float* incl, float* excl, float* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  float x = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  float xprev = __shfl_up(x, 1);
+  const float x = wave_incl_scan(v);
+  const float xprev = __shfl_up(x, 1);
   __syncthreads();
   if (lane == 63) red[wv] = x;
   __syncthreads();
@@ -410,15 +482,6 @@ __device__ inline int next_child(const uint64_t (*cm)[kMaxT / 64], int n, int af
   }
 }
 
-// Wave-wide sum and maximum (every lane gets the result).
-__device__ inline float wave_sum(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-__device__ inline float wave_max(float v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
@@ -513,16 +576,23 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
     }
 
     int n = 0, path_len = 0, passes = 0, emitted = -1, owner = -1;
+    int raw_row = 0;   // the node whose chunk `raw` holds: the root's, loaded at the start
     bool sync_ok = true, nonfinite = false;
     while (st == SV_TREE_OK) {
       const float* qrow = greedy ? nullptr : p.q_probs + (rowbase + n) * p.V;
-      // ---- statistics of node n's row: every chunk, one exchange (the
-      // root's chunk was loaded at the start)
-      if (n != 0) load_raw<BF16, VEC>(logits_row(rowbase + n), c0, c1, raw);
+      // ---- statistics of node n's row: every chunk, one exchange
+      if (raw_row != n) load_raw<BF16, VEC>(logits_row(rowbase + n), c0, c1, raw);
       {
         const float4 loc = chunk_stats<BF16, VEC>(raw, c0, c1, greedy, k, pc, red_m, red_s, red_i, red_f);
         if (tid == 0) { pubv[0] = loc.x; pubv[1] = loc.y; pubv[2] = loc.z; }
         if (!gx.exchange(w, pubv, 3, xv)) { sync_ok = false; break; }
+        // The first child is the likeliest next node (tried first; in greedy
+        // trees the drafter's best token): its chunk loads go out now, under
+        // the combine and the acceptance test.  (After the exchange, so that
+        // the exchange's polls, which complete in order with earlier loads,
+        // do not wait for them.)
+        raw_row = next_child(cm_s, n, n, W);
+        if (raw_row >= 0) load_raw<BF16, VEC>(logits_row(rowbase + raw_row), c0, c1, raw);
         // combined over the chunks by the first wave, one lane per chunk
         if (tid < 64) {
           const bool live = tid < p.nchunk;
@@ -687,11 +757,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
             // the first wave scans that segment, one entry per lane
             const int i = ts * 64 + tid;
             const float v = i < len ? resid(i) : 0.f;
-            float x = v;
-            for (int off = 1; off < 64; off <<= 1) {
-              const float u = __shfl_up(x, off);
-              if (tid >= off) x += u;
-            }
+            const float x = wave_incl_scan(v);
             const float base = cum + excl_b;
             const uint64_t over = __ballot(base + x > target);
             const uint64_t pos = __ballot(v > 0.f);
