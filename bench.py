@@ -200,6 +200,30 @@ def back_to_back(devs, k, stream):
     return a.elapsed_time(b) / k
 
 
+def in_step_times(devs, k, stream):
+    """Mean duration (ms) of each kernel of the step in the step's own setting:
+    k steps, each issued as its three entry points (mask, attention, accept)
+    with HIP events around each call on the launch stream, cycling over the
+    input sets in ``devs``."""
+    import numpy as np
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(k)]
+    torch.cuda.synchronize()
+    for i, e in enumerate(evs):
+        d = devs[i % len(devs)]
+        e[0].record(stream)
+        d.mask_build()
+        e[1].record(stream)
+        d.tree_attn()
+        e[2].record(stream)
+        d.spec_accept()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    return {"tree_mask_build": float(t[:, 0].mean()), "tree_attn": float(t[:, 1].mean()),
+            "spec_accept": float(t[:, 2].mean())}
+
+
 def prewarm(devs, seconds):
     """Verification steps back to back for about ``seconds`` of wall time,
     untimed, so that the timed steps run at the clock and power state the GPU
@@ -353,7 +377,7 @@ def cpu_baseline(inst, seconds):
 
 def all_workloads(steps):
     """One line per workload: the verify step (median of single steps between
-    HIP events), attention and accept launches timed apart, attention against
+    HIP events), attention and accept timed inside steps, attention against
     the bf16 MFMA peak (the fp32 workload against the fp32 vector peak) and
     HBM, and the walk against reading every tree row's logits once at peak."""
     import numpy as np
@@ -368,8 +392,8 @@ def all_workloads(steps):
         dev = DeviceProblem(inst, device="cuda:0")
         prewarm((dev,), 1.0)
         step = step_distribution((dev,), steps, stream)
-        attn_ms = time_launches(dev.tree_attn, steps, stream)
-        acc_ms = time_launches(dev.spec_accept, steps, stream)
+        ins = in_step_times((dev,), steps, stream)
+        attn_ms, acc_ms = ins["tree_attn"], ins["spec_accept"]
         res = dev.accept_results()
         flops, attn_bytes = algorithmic_work(inst)
         peak = MFMA_BF16_PEAK_TFLOPS if inst.dtype == "bf16" else 157.3
@@ -474,16 +498,19 @@ def main():
           file=sys.stderr, flush=True)
 
     # the distribution of single steps (events around each step, same
-    # alternation), then the same input set every step (warm caches)
+    # alternation), each kernel's duration inside steps, then the same input
+    # set every step (warm caches)
     per_step = step_distribution(devs, args.steps, stream)
+    n = max(200, args.steps)   # ~0.12 s: enough launches for a stable mean
+    in_step = in_step_times(devs, n, stream)
     warm_ms = back_to_back((dev,), args.steps, stream)
     del other, devs
     torch.cuda.empty_cache()
 
-    n = max(10, args.steps)
-    mask_ms = time_launches(dev.mask_build, n, stream)
-    attn_ms = time_launches(dev.tree_attn, n, stream)
-    acc_ms = time_launches(dev.spec_accept, n, stream)
+    mask_ms, attn_ms, acc_ms = in_step["tree_mask_build"], in_step["tree_attn"], in_step["spec_accept"]
+    # attention launched back to back on its own (no walk between launches:
+    # the chip runs it at a lower clock than inside steps), for context
+    attn_alone_ms = time_launches(dev.tree_attn, n, stream)
     res = dev.accept_results()
     # the commit of the accepted path (not part of the step): into caches with
     # room after the prefix, so the step's own caches stay as they are
@@ -506,7 +533,10 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": "k_attn_bf16 (sv_tree_attn)",
-                "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(attn_ms, 5)}
+                "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(attn_ms, 5),
+                "launch_timing": "mean of HIP events around each sv_tree_attn call inside steps issued as "
+                                 "mask, attention, accept (inputs alternating as in the timed steps)",
+                "avg_launch_ms_back_to_back": round(attn_alone_ms, 5)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -532,7 +562,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_ms": {"tree_mask_build": round(mask_ms, 5), "tree_attn": round(attn_ms, 5),
-                       "spec_accept": round(acc_ms, 5)},
+                       "spec_accept": round(acc_ms, 5), "note": "inside steps (each entry point between events)"},
         "inputs": "two input sets alternating (no step finds its inputs in the caches)",
         "prewarm": {"ms": round(pw_ms, 1), "steps": pw_steps},
         "per_step": per_step,
