@@ -727,7 +727,9 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
           float va[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int i = s0 + 4 * j;
+            // segments lie 256 bytes apart: each thread starts at its own
+            // quad, so the 16 lanes of a bank row read 16 different banks
+            const int i = s0 + 4 * ((j + tid) & 15);
             if (i + 4 <= len) {
               const float4 pp = *reinterpret_cast<const float4*>(pc + i);
               if (have_q) {
