@@ -16,9 +16,9 @@
 //            A = K rows from LDS, B = Q held in registers for the whole run;
 //   softmax  online, fp32: the MFMA yields raw dot products of the bf16 q and
 //            k as stored, and the score scale times log2(e) is applied to them
-//            in fp32 right before exp2; the running max is only raised when a
-//            block's max exceeds it by more than 8 (log2 units), so the O
-//            rescale is rare and exp2 arguments stay <= 8;
+//            in fp32 right before exp2; each row's offset is only raised when
+//            a block's row sum of P shows a score more than 64 (log2 units)
+//            past it, so the O rescale is rare and every P stays below 2^64;
 //   output   O^T[d][row] += V^T[d][key] P^T[key][row]: B = P taken straight
 //            from the score registers; A = V^T read from the row-major V tile
 //            with ds_read_b64_tr_b16 (each 16-lane group gathers 4 keys x 16
@@ -263,7 +263,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // mu: the running offset of the lane's row in raw dot-product units,
   // subtracted by the score MFMA itself (its accumulator starts at
   // cinit = -mu); valid once a visible key has set it.  With c = scale *
-  // log2(e), P = 2^(c (dot - mu)) with c (dot - mu) <= 8 kept.
+  // log2(e), P = 2^(c (dot - mu)); a raise puts the new offset at the block's
+  // maximum when that exceeds the old one by more than 8 / c.
   f32x4 acc[NT][DT], cinit[NT];
   float mu[NT], lsum[NT];
   bool valid[NT];
