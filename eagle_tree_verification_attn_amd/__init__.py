@@ -27,7 +27,7 @@ SV_SIB_WITHOUT_REPLACEMENT, SV_SIB_IID = 0, 1
 EXPORTS = ["sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_verify_step_noalloc",
            "sv_commit_accepted", "sv_workspace_bytes", "sv_status_string", "sv_last_error",
            "sv_eagle2_state_bytes", "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish",
-           "sv_draft_head"]
+           "sv_eagle2_expand_finish", "sv_draft_head"]
 
 
 class SvTree(ctypes.Structure):
@@ -122,6 +122,9 @@ def lib():
         L.sv_eagle2_finish.argtypes = [P(SvEagle2Cfg), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]
+        L.sv_eagle2_expand_finish.argtypes = [P(SvEagle2Cfg), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.sv_draft_head.argtypes = [P(SvHeadArgs), ctypes.c_void_p]
         L.sv_workspace_bytes.argtypes = [P(SvTree), P(SvAttnArgs), P(SvAcceptArgs)]
         L.sv_workspace_bytes.restype = ctypes.c_size_t
@@ -131,7 +134,8 @@ def lib():
         L.sv_last_error.restype = ctypes.c_char_p
         for f in ("sv_tree_mask_build", "sv_tree_attn", "sv_spec_accept", "sv_verify_step", "sv_verify_step_noalloc",
                   "sv_commit_accepted",
-                  "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish", "sv_draft_head"):
+                  "sv_eagle2_begin", "sv_eagle2_expand", "sv_eagle2_finish", "sv_eagle2_expand_finish",
+                  "sv_draft_head"):
             getattr(L, f).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -272,6 +276,14 @@ def sv_eagle2_finish(cfg, state, parent, tokens, num_nodes, q_row, status, strea
     return _check(lib().sv_eagle2_finish(ctypes.byref(cfg), _ptr(state), _nbytes(state), _ptr(parent), _ptr(tokens),
                                          _ptr(num_nodes), _ptr(q_row), _ptr(status), _stream(stream)),
                   "sv_eagle2_finish", raise_on_error)
+
+
+def sv_eagle2_expand_finish(cfg, state, step, q, parent, tokens, num_nodes, q_row, status, stream=None,
+                            raise_on_error=True):
+    return _check(lib().sv_eagle2_expand_finish(ctypes.byref(cfg), _ptr(state), _nbytes(state), int(step), _ptr(q),
+                                                _ptr(parent), _ptr(tokens), _ptr(num_nodes), _ptr(q_row),
+                                                _ptr(status), _stream(stream)),
+                  "sv_eagle2_expand_finish", raise_on_error)
 
 
 def make_head_args(h, B, A_sh, perm, W, u, cand_ids, cand_logits, tile, k_tile):

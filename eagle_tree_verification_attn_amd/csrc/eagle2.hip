@@ -22,6 +22,8 @@
 //                  next frontier.
 //   k_finish       one workgroup per sequence: ranks every draft node, keeps
 //                  the m best and assigns flattened positions depth by depth.
+//   k_expand_finish  the last step's k_expand and k_finish in one workgroup
+//                  per sequence (one launch less).
 //
 // The per-sequence kernels are latency-bound: each issues all of its
 // independent loads at once (one HBM round trip) and then works in LDS.
@@ -281,8 +283,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(E2Params p, const flo
 // trip: the sequence's state, its frontier records, the chunks' range flags of
 // all k rows and the first group of chunk keys (all inside the state whatever
 // the frontier's size; only the frontier's rows are used).
-__global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int32_t* frontier_out,
-                                                       int32_t* frontier_tokens) {
+__device__ inline void expand_body(const E2Params& p, int step, int32_t* frontier_out, int32_t* frontier_tokens) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   int32_t* s = p.seq + (size_t)b * 8;
@@ -412,10 +413,14 @@ __global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int
   }
 }
 
+__global__ __launch_bounds__(kE2Threads) void k_expand(E2Params p, int step, int32_t* frontier_out,
+                                                       int32_t* frontier_tokens) {
+  expand_body(p, step, frontier_out, frontier_tokens);
+}
+
 // ---------------------------------------------------------------- finish
-__global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* parent_out, int32_t* tokens_out,
-                                                           int32_t* num_nodes, int32_t* q_row_out,
-                                                           int32_t* status_out) {
+__device__ inline void finish_body(const E2Params& p, int32_t* parent_out, int32_t* tokens_out, int32_t* num_nodes,
+                                   int32_t* q_row_out, int32_t* status_out) {
   constexpr int kMaxNodes = 2048;
   __shared__ uint64_t nkey_s[kMaxNodes];   // (value, shallower, earlier): larger ranks first
   __shared__ int rnk_s[kMaxNodes];
@@ -540,6 +545,25 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* 
   if (tid == 0) num_nodes[b] = T;
 }
 
+__global__ __launch_bounds__(kFinishThreads) void k_finish(E2Params p, int32_t* parent_out, int32_t* tokens_out,
+                                                           int32_t* num_nodes, int32_t* q_row_out,
+                                                           int32_t* status_out) {
+  finish_body(p, parent_out, tokens_out, num_nodes, q_row_out, status_out);
+}
+
+// The last expansion step and the rerank in one launch: the workgroup of a
+// sequence appends the last layer, and after a barrier (its own global
+// writes are then visible to all of its threads) reads the whole tree back
+// and flattens it.  Saves the finish kernel's launch and its load round trip.
+static_assert(kE2Threads == kFinishThreads, "one block size for the fused kernel");
+__global__ __launch_bounds__(kE2Threads) void k_expand_finish(E2Params p, int step, int32_t* parent_out,
+                                                              int32_t* tokens_out, int32_t* num_nodes,
+                                                              int32_t* q_row_out, int32_t* status_out) {
+  expand_body(p, step, nullptr, nullptr);
+  __syncthreads();
+  finish_body(p, parent_out, tokens_out, num_nodes, q_row_out, status_out);
+}
+
 // ---------------------------------------------------------------- launchers
 sv_status launch_eagle2_begin(const sv_eagle2_cfg* c, void* state, const int32_t* root_tokens, hipStream_t s) {
   const E2Layout L = eagle2_layout(c);
@@ -563,6 +587,23 @@ sv_status launch_eagle2_expand(const sv_eagle2_cfg* c, void* state, int step, co
   hipLaunchKernelGGL(k_expand, dim3(c->B), dim3(kE2Threads), 0, s, p, step, frontier, frontier_tokens);
   e = hipGetLastError();
   if (e != hipSuccess) { set_error("eagle2 expand launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  return SV_OK;
+}
+
+sv_status launch_eagle2_expand_finish(const sv_eagle2_cfg* c, void* state, int step, const float* q, int32_t* parent,
+                                      int32_t* tokens, int32_t* num_nodes, int32_t* q_row, int32_t* status,
+                                      hipStream_t s) {
+  const E2Layout L = eagle2_layout(c);
+  const E2Params p = make_params(c, L, state);
+  if (c->B == 0) return SV_OK;
+  const int jrows = step == 0 ? 1 : c->k;
+  hipLaunchKernelGGL(k_row_topk, dim3(c->B * jrows * L.nsplit), dim3(kTopkThreads), 0, s, p, q, jrows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) { set_error("eagle2 top-k launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
+  hipLaunchKernelGGL(k_expand_finish, dim3(c->B), dim3(kE2Threads), 0, s, p, step, parent, tokens, num_nodes, q_row,
+                     status);
+  e = hipGetLastError();
+  if (e != hipSuccess) { set_error("eagle2 expand+finish launch: %s", hipGetErrorString(e)); return SV_E_HIP; }
   return SV_OK;
 }
 

@@ -327,6 +327,25 @@ sv_status sv_eagle2_expand(const sv_eagle2_cfg* c, void* state, size_t state_byt
   return launch_eagle2_expand(c, state, step, q, frontier, frontier_tokens, (hipStream_t)stream);
 }
 
+sv_status sv_eagle2_expand_finish(const sv_eagle2_cfg* c, void* state, size_t state_bytes, int32_t step,
+                                  const float* q, int32_t* parent, int32_t* tokens, int32_t* num_nodes,
+                                  int32_t* q_row, int32_t* status, void* stream) {
+  clear_error();
+  sv_status st;
+  if ((st = check_eagle2(c))) return st;
+  if (step < 0 || step >= c->depth) { set_error("step %d outside [0, %d)", step, c->depth); return SV_E_SHAPE; }
+  if (c->B == 0) return SV_OK;
+  if ((st = check_state(c, state, state_bytes))) return st;
+  if (!q) { set_error("q is NULL"); return SV_E_NULL; }
+  if (!aligned(q, 16)) { set_error("q must be 16-byte aligned"); return SV_E_UNSUPPORTED; }
+  if (!parent || !tokens || !num_nodes || !q_row || !status) {
+    set_error("parent/tokens/num_nodes/q_row/status is NULL");
+    return SV_E_NULL;
+  }
+  return launch_eagle2_expand_finish(c, state, step, q, parent, tokens, num_nodes, q_row, status,
+                                     (hipStream_t)stream);
+}
+
 sv_status sv_eagle2_finish(const sv_eagle2_cfg* c, const void* state, size_t state_bytes, int32_t* parent,
                            int32_t* tokens, int32_t* num_nodes, int32_t* q_row, int32_t* status, void* stream) {
   clear_error();

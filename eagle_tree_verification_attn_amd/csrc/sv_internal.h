@@ -109,6 +109,9 @@ E2Layout eagle2_layout(const sv_eagle2_cfg* c);
 sv_status launch_eagle2_begin(const sv_eagle2_cfg* c, void* state, const int32_t* root_tokens, hipStream_t s);
 sv_status launch_eagle2_expand(const sv_eagle2_cfg* c, void* state, int step, const float* q, int32_t* frontier,
                                int32_t* frontier_tokens, hipStream_t s);
+sv_status launch_eagle2_expand_finish(const sv_eagle2_cfg* c, void* state, int step, const float* q, int32_t* parent,
+                                      int32_t* tokens, int32_t* num_nodes, int32_t* q_row, int32_t* status,
+                                      hipStream_t s);
 sv_status launch_eagle2_finish(const sv_eagle2_cfg* c, const void* state, int32_t* parent, int32_t* tokens,
                                int32_t* num_nodes, int32_t* q_row, int32_t* status, hipStream_t s);
 

@@ -8,7 +8,8 @@ the current torch stream.  Nothing here computes any part of the verification.
 import numpy as np
 
 from . import (SV_SIB_IID, SV_SIB_WITHOUT_REPLACEMENT, SvEagle2Cfg, make_accept_args, make_attn_args,
-               make_commit_args, make_tree, sv_commit_accepted, sv_eagle2_begin, sv_eagle2_expand, sv_eagle2_finish,
+               make_commit_args, make_tree, sv_commit_accepted, sv_eagle2_begin, sv_eagle2_expand,
+               sv_eagle2_expand_finish, sv_eagle2_finish,
                sv_eagle2_state_bytes, sv_spec_accept, sv_tree_attn, sv_tree_mask_build, sv_verify_step,
                sv_workspace_bytes)
 
@@ -151,12 +152,19 @@ class DeviceTreeBuilder:
         self.num_nodes = torch.full((B,), -7, **i32)
         self.status = torch.full((B,), -7, **i32)
 
-    def run(self, q_steps, root_tokens, stream=None):
+    def run(self, q_steps, root_tokens, stream=None, fused_last=False):
+        """fused_last: the last step and the finish in one call
+        (sv_eagle2_expand_finish); that step's frontier is then not written."""
         sv_eagle2_begin(self.cfg, self.state, root_tokens, stream)
-        for s in range(self.cfg.depth):
+        last = self.cfg.depth - 1
+        for s in range(self.cfg.depth if not fused_last else last):
             sv_eagle2_expand(self.cfg, self.state, s, q_steps[s], self.frontier[s], self.frontier_tokens[s], stream)
-        sv_eagle2_finish(self.cfg, self.state, self.parent, self.tokens, self.num_nodes, self.q_row, self.status,
-                         stream)
+        if fused_last:
+            sv_eagle2_expand_finish(self.cfg, self.state, last, q_steps[last], self.parent, self.tokens,
+                                    self.num_nodes, self.q_row, self.status, stream)
+        else:
+            sv_eagle2_finish(self.cfg, self.state, self.parent, self.tokens, self.num_nodes, self.q_row, self.status,
+                             stream)
 
     def results(self):
         return dict(parent=self.parent.cpu().numpy(), tokens=self.tokens.cpu().numpy(),

@@ -277,7 +277,8 @@ sv_status sv_commit_accepted(const sv_tree* tree, int32_t* tree_status, const in
  *
  * Use: sv_eagle2_begin, then for step = 0 .. depth-1 run the drafter on the
  * current frontier (the root at step 0) and call sv_eagle2_expand with its
- * probability rows, then sv_eagle2_finish.  All calls only enqueue work on the
+ * probability rows, then sv_eagle2_finish (or, for the last step,
+ * sv_eagle2_expand_finish, which does both).  All calls only enqueue work on the
  * stream; the state lives in one caller buffer of sv_eagle2_state_bytes bytes
  * (256-byte aligned), and calls on one state must be in this order. */
 typedef struct {
@@ -319,6 +320,16 @@ sv_status sv_eagle2_expand(const sv_eagle2_cfg* c, void* state, size_t state_byt
 sv_status sv_eagle2_finish(const sv_eagle2_cfg* c, const void* state, size_t state_bytes,
                            int32_t* parent, int32_t* tokens, int32_t* num_nodes, int32_t* q_row,
                            int32_t* status, void* stream);
+
+/* sv_eagle2_expand followed by sv_eagle2_finish, with the same arguments and
+ * results, in one launch after the row top-k: the workgroup that appends a
+ * sequence's last layer also reranks and flattens its tree, so the finish
+ * needs no launch and no second read of the state.  Meant for the last step
+ * (step = depth - 1); the next frontier is not written.  Same errors as the
+ * two calls (checked before anything is enqueued). */
+sv_status sv_eagle2_expand_finish(const sv_eagle2_cfg* c, void* state, size_t state_bytes, int32_t step,
+                                  const float* q, int32_t* parent, int32_t* tokens, int32_t* num_nodes,
+                                  int32_t* q_row, int32_t* status, void* stream);
 
 /* ---------------------------------------------------------------- draft head
  * Two-stage draft LM head ([EAGLE-4 blog], sections "EAGLE Efficient LM

@@ -158,6 +158,17 @@ def test_eagle2_entry_points_reject_bad_host_arguments():
     assert L.sv_eagle2_expand(ctypes.byref(c), fake, need, 0, odd, None, None, None) == sv.SV_E_UNSUPPORTED
     # finish: every output is required
     assert L.sv_eagle2_finish(ctypes.byref(c), fake, need, fake, fake, fake, fake, None, None) == sv.SV_E_NULL
+    # expand + finish: the checks of both
+    assert L.sv_eagle2_expand_finish(ctypes.byref(c), fake, need, 6, fake, fake, fake, fake, fake, fake,
+                                     None) == sv.SV_E_SHAPE
+    assert L.sv_eagle2_expand_finish(ctypes.byref(c), fake, need, 5, None, fake, fake, fake, fake, fake,
+                                     None) == sv.SV_E_NULL
+    assert L.sv_eagle2_expand_finish(ctypes.byref(c), fake, need, 5, odd, fake, fake, fake, fake, fake,
+                                     None) == sv.SV_E_UNSUPPORTED
+    assert L.sv_eagle2_expand_finish(ctypes.byref(c), fake, need, 5, fake, fake, None, fake, fake, fake,
+                                     None) == sv.SV_E_NULL
+    assert L.sv_eagle2_expand_finish(ctypes.byref(c), fake, need - 1, 5, fake, fake, fake, fake, fake, fake,
+                                     None) == sv.SV_E_WORKSPACE
     bad = _e2(k=0)
     assert L.sv_eagle2_finish(ctypes.byref(bad), fake, need, fake, fake, fake, fake, fake, None) == sv.SV_E_SHAPE
     # B = 0: nothing to do, no pointer is looked at

@@ -20,13 +20,13 @@ from synth import make_draft_rows
 pytestmark = pytest.mark.gpu
 
 
-def _run(B, V, k, depth, m, q_host, roots):
+def _run(B, V, k, depth, m, q_host, roots, fused=False):
     import torch
     from eagle_tree_verification_attn_amd.problem import DeviceTreeBuilder
     dev = DeviceTreeBuilder(B, V, k, depth, m)
     q_dev = [torch.from_numpy(np.ascontiguousarray(q)).cuda() for q in q_host]
     roots_dev = torch.from_numpy(np.asarray(roots, dtype=np.int32)).cuda()
-    dev.run(q_dev, roots_dev)
+    dev.run(q_dev, roots_dev, fused_last=fused)
     torch.cuda.synchronize()
     return dev.results()
 
@@ -60,18 +60,24 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["finish", "fused_last"])
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_V{c[1]}_k{c[2]}_d{c[3]}_m{c[4]}{'_ties' if c[5] else ''}" for c in CASES])
-def test_builder_matches_oracle(case):
+def test_builder_matches_oracle(case, fused):
+    """fused: the last step runs as sv_eagle2_expand_finish (expand and finish
+    in one launch); every output must be the same."""
     need_gpu()
     B, V, k, depth, m, tie = case
     q = make_draft_rows(B, k, depth, V, seed=sum(case[:5]), tie_step=tie)
     roots = np.arange(B, dtype=np.int32) % V
-    say(f"eagle2 B={B} V={V} k={k} depth={depth} m={m} ties={tie}")
+    say(f"eagle2 B={B} V={V} k={k} depth={depth} m={m} ties={tie} fused={fused}")
     ref = eagle2.build(q, roots, k, depth, m)
-    res = _run(B, V, k, depth, m, q, roots)
+    res = _run(B, V, k, depth, m, q, roots, fused)
     _check(res, ref, label=str(case))
-    # the frontier tokens are the frontier nodes' tokens
-    assert (res["frontier_tokens"][res["frontier"] < 0] == -1).all()
+    # the frontier tokens are the frontier nodes' tokens (the fused last step
+    # writes no frontier)
+    steps = depth - 1 if fused else depth
+    fr, ft = res["frontier"][:steps], res["frontier_tokens"][:steps]
+    assert (ft[fr < 0] == -1).all()
 
 
 @pytest.mark.parametrize("V", [20000, 9001])
@@ -101,7 +107,8 @@ def test_builder_heavy_ties(V):
     assert sorted(kids.tolist()) == list(range(k))
 
 
-def test_invalid_rows_mark_only_their_sequence():
+@pytest.mark.parametrize("fused", [False, True], ids=["finish", "fused_last"])
+def test_invalid_rows_mark_only_their_sequence(fused):
     need_gpu()
     B, V, k, depth, m = 6, 800, 3, 3, 10
     q = make_draft_rows(B, k, depth, V, seed=77)
@@ -114,7 +121,7 @@ def test_invalid_rows_mark_only_their_sequence():
     say("eagle2 invalid rows")
     ref = eagle2.build(q, roots, k, depth, m)
     assert ref["status"].tolist() == [0, 10, 10, 10, 0, 10]
-    res = _run(B, V, k, depth, m, q, roots)
+    res = _run(B, V, k, depth, m, q, roots, fused)
     _check(res, ref, label="invalid")
     assert (res["parent"][1] == -1).all() and res["num_nodes"][1] == 0
 
@@ -127,6 +134,9 @@ def test_builder_full_workload_sampled():
     roots = (np.arange(B, dtype=np.int32) * 7919) % V
     say(f"eagle2 full workload B={B} V={V} k={k} depth={depth} m={m}")
     res = _run(B, V, k, depth, m, q, roots)
+    fused = _run(B, V, k, depth, m, q, roots, fused=True)
+    for f in ("parent", "tokens", "q_row", "num_nodes", "status"):
+        np.testing.assert_array_equal(fused[f], res[f], err_msg=f"fused last step: {f}")
     seqs = [0, 5, 13, 31]
     for b in seqs:
         r = eagle2.build_sequence([q[s][b] for s in range(depth)], int(roots[b]), k, depth, m)
