@@ -37,7 +37,7 @@
 
 namespace sv {
 
-constexpr int kAccThreads = 256;
+constexpr int kAccThreads = 512;
 constexpr int kMaxChunk = 16384;  // vocabulary entries one walk workgroup caches in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -81,8 +81,11 @@ __device__ inline bool greedy_temp(float tau) { return !(tau > 0.f); }
 // before any arithmetic: thread t takes kBatch groups of 8 entries at
 // c0 + 8 t + 8 q * threads (q < kBatch); addresses past the chunk end are
 // clamped to the chunk start, so every load is unconditional.
-constexpr int kBatch = 8;
+constexpr int kBatch = kMaxChunk / (kAccThreads * 8);
 static_assert(kAccThreads * 8 * kBatch == kMaxChunk, "chunk covered by one batch");
+static_assert(kAccThreads >= kMaxT, "one tree position per thread");
+constexpr int kSeg = kMaxChunk / kAccThreads;   // chunk entries per thread in the draw
+static_assert(kSeg % 16 == 0 && kSeg <= 64, "draw segments: whole quads, at most one entry per lane in the final scan");
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <bool BF16, int H>
@@ -531,6 +534,17 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
     // bounds whatever the sequence's status.)
     u32x4 raw[kBatch][RH];
     load_raw<BF16, VEC>(logits_row(rowbase), c0, c1, raw);
+    // The tree data of position tid goes out in the same round trip, before
+    // the sequence's status and size are known (the arrays are [B][T_max],
+    // so these loads are in bounds).
+    int x_r = 0, par_r = -1;
+    float ua_r = 0.f, us_r = 0.f;
+    if (tid < p.T_max) {
+      x_r = p.tokens[rowbase + tid];
+      par_r = p.parent[rowbase + tid];
+      ua_r = p.u_accept[rowbase + tid];
+      us_r = p.u_sample[rowbase + tid];
+    }
     int st = p.status[b];
     const int Tb = p.num_nodes[b];
     if (st == SV_TREE_OK && (Tb < 1 || Tb > p.T_max)) st = SV_TREE_E_COUNT;
@@ -546,34 +560,35 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       for (int i = tid; i < Tb * (kMaxT / 64); i += kAccThreads) cm_s[i / (kMaxT / 64)][i % (kMaxT / 64)] = 0ull;
     __syncthreads();
     if (st == SV_TREE_OK) {
-      // round 1: tree (as child bit rows), tokens, uniforms.  A valid tree
-      // has 0 <= parent[c] < c for 1 <= c < T_b.
-      for (int i = tid; i < Tb; i += kAccThreads) {
-        const int x = p.tokens[rowbase + i];
-        tok_s[i] = x;
-        ua_s[i] = p.u_accept[rowbase + i];
-        us_s[i] = p.u_sample[rowbase + i];
-        if (i > 0) {
-          const int par = p.parent[rowbase + i];
-          if (par >= 0 && par < i) atomicOr(reinterpret_cast<unsigned long long*>(&cm_s[par][i >> 6]), 1ull << (i & 63));
+      // the tree (as child bit rows), tokens, uniforms.  A valid tree has
+      // 0 <= parent[c] < c for 1 <= c < T_b.
+      if (tid < Tb) {
+        tok_s[tid] = x_r;
+        ua_s[tid] = ua_r;
+        us_s[tid] = us_r;
+        if (tid > 0) {
+          if (par_r >= 0 && par_r < tid)
+            atomicOr(reinterpret_cast<unsigned long long*>(&cm_s[par_r][tid >> 6]), 1ull << (tid & 63));
           else atomicOr(&flags_s, 2);   // only a caller's own status could let such a tree through
-          if (x < 0 || x >= p.V) atomicOr(&flags_s, 1);   // the root's token is not read
+          if (x_r < 0 || x_r >= p.V) atomicOr(&flags_s, 1);   // the root's token is not read
         }
       }
       __syncthreads();
       if (flags_s & 2) st = SV_TREE_E_PARENT;
       else if (flags_s & 1) st = SV_TREE_E_TOKEN;
       else if (!greedy && p.q_probs == nullptr) st = SV_TREE_E_NOQ;
-      // round 2: each candidate's logit and draft probability in its parent's row
-      if (st == SV_TREE_OK && !greedy) {
-        for (int c = 1 + tid; c < Tb; c += kAccThreads) {
-          const int n = p.parent[rowbase + c], x = tok_s[c];
-          zx_s[c] = load_logit(logits_row(rowbase + n), (size_t)x, BF16);
-          qx_s[c] = p.q_probs[(rowbase + n) * p.V + x];
-        }
-      }
-      __syncthreads();
     }
+    // Each candidate's logit and draft probability in its parent's row (a
+    // second, dependent round trip): the loads go out now and land in
+    // registers; they are put in LDS after the root's statistics pass, which
+    // covers their latency, and read only after the first exchange.
+    const bool has_x = st == SV_TREE_OK && !greedy && tid >= 1 && tid < Tb;
+    float zx_r = 0.f, qx_r = 0.f;
+    if (has_x) {
+      zx_r = load_logit(logits_row(rowbase + par_r), (size_t)x_r, BF16);
+      qx_r = p.q_probs[(rowbase + par_r) * p.V + x_r];
+    }
+    bool x_pending = true;
 
     int n = 0, path_len = 0, passes = 0, emitted = -1, owner = -1;
     int raw_row = 0;   // the node whose chunk `raw` holds: the root's, loaded at the start
@@ -584,6 +599,13 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       if (raw_row != n) load_raw<BF16, VEC>(logits_row(rowbase + n), c0, c1, raw);
       {
         const float4 loc = chunk_stats<BF16, VEC>(raw, c0, c1, greedy, k, pc, red_m, red_s, red_i, red_f);
+        if (x_pending) {   // visible after the exchange's barriers, before any test reads them
+          if (has_x) {
+            zx_s[tid] = zx_r;
+            qx_s[tid] = qx_r;
+          }
+          x_pending = false;
+        }
         if (tid == 0) { pubv[0] = loc.x; pubv[1] = loc.y; pubv[2] = loc.z; }
         if (!gx.exchange(w, pubv, 3, xv)) { sync_ok = false; break; }
         // The first child is the likeliest next node (tried first; in greedy
@@ -658,7 +680,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
           __syncthreads();
           have_q = true;
         }
-        // thread t sums entries 4t + 1024 j, j = 0..15, in four chains
+        // thread t sums entries 4 t + 4 kAccThreads j in four chains
         float pa[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kMaxChunk / (4 * kAccThreads); ++j) {
@@ -720,16 +742,16 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
       if (w == owner) {
         // residual entry i of the chunk (q is only needed after a rejection)
         auto resid = [&](int i) { return have_q ? fmaxf(fmaf(-Adraw, qc[i], pc[i] * f), 0.f) : pc[i] * f; };
-        // thread t owns the 64 entries [64 t, 64 t + 64) of the chunk
-        const int s0 = tid * 64;
+        // thread t owns the kSeg entries [kSeg t, kSeg t + kSeg) of the chunk
+        const int s0 = tid * kSeg;
         int y = -1;
         if (!fallback) {
           float va[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            // segments lie 256 bytes apart: each thread starts at its own
-            // quad, so the 16 lanes of a bank row read 16 different banks
-            const int i = s0 + 4 * ((j + tid) & 15);
+          for (int j = 0; j < kSeg / 4; ++j) {
+            // segments lie 4 kSeg bytes apart: each thread starts at its own
+            // quad, so the lanes of a bank row read different banks
+            const int i = s0 + 4 * ((j + tid) & (kSeg / 4 - 1));
             if (i + 4 <= len) {
               const float4 pp = *reinterpret_cast<const float4*>(pc + i);
               if (have_q) {
@@ -756,9 +778,10 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
           __syncthreads();
           const int ts = ibcast;
           if (ts != 0x7FFFFFFF && tid < 64) {
-            // the first wave scans that segment, one entry per lane
-            const int i = ts * 64 + tid;
-            const float v = i < len ? resid(i) : 0.f;
+            // the first wave scans that segment, one entry per lane (lanes
+            // past the segment add nothing)
+            const int i = ts * kSeg + tid;
+            const float v = (tid < kSeg && i < len) ? resid(i) : 0.f;
             const float x = wave_incl_scan(v);
             const float base = cum + excl_b;
             const uint64_t over = __ballot(base + x > target);
@@ -766,7 +789,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
             int hit = -1;
             if (over) hit = (int)__ffsll((unsigned long long)over) - 1;
             else if (pos) hit = 63 - __clzll((long long)pos);   // rounding left no crossing: the last entry with mass
-            if (tid == 0) ybcast = hit >= 0 ? c0 + ts * 64 + hit : -1;
+            if (tid == 0) ybcast = hit >= 0 ? c0 + ts * kSeg + hit : -1;
           } else if (ts == 0x7FFFFFFF && tid == 0) {
             ybcast = -1;
           }
@@ -776,7 +799,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept_walk(WalkParams p) {
         if (y < 0) {
           // no crossing at all: the largest entry of the chunk with positive mass
           int lp = -1;
-          for (int i = s0; i < min(s0 + 64, len); ++i)
+          for (int i = s0; i < min(s0 + kSeg, len); ++i)
             if (resid(i) > 0.f) lp = c0 + i;
           __syncthreads();
           if (tid == 0) ibcast = -1;
