@@ -31,6 +31,7 @@
 // them with the log-sum-exp rule.
 #include "sv_internal.h"
 
+#include <algorithm>
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -50,10 +51,13 @@ struct AttnParams {
   const int32_t* status;
   const uint64_t* anc;
   void* out;
-  float* part_o;   // [B][T_max][Hq][lsplit][D]
-  float* part_ml;  // [B][T_max][Hq][lsplit][2]
+  float* part_o;   // [B][T_max][Hq][n][D], n = the key split in use (room for lstride)
+  float* part_ml;  // [B][T_max][Hq][n][2]
+  int32_t* dyn_ls; // the key split a sizes-driven plan chose (read by the merge)
   int B, T_max, Hq, Hkv, G, L_max, W;
   int rows_per_wg, msplit, lsplit, chunk;
+  int lstride;     // partials per row the workspace holds: lsplit, or ls_cap with dyn
+  int dyn, ls_cap, keys_max;   // sizes-driven plan (see decode_work)
   int remap;
   float scale_log2;  // score scale * log2(e), applied in fp32
   float raise_raw;   // 8 / scale_log2: the offset-raise bound in raw dot-product units
@@ -68,6 +72,110 @@ __device__ inline int logical_block(int remap) {
   if (!remap) return i;
   const int per = gridDim.x >> 3;
   return (i & 7) * per + (i >> 3);
+}
+
+// Row blocks (of rows_per_wg query rows) of a sequence that hold valid rows.
+__device__ inline int seq_row_blocks(const AttnParams& p, int st, int Tb, int Lb) {
+  const bool ok = st == SV_TREE_OK && Tb >= 1 && Tb <= p.T_max && Lb >= 0 && Lb <= p.L_max;
+  return ok ? (Tb * p.G + p.rows_per_wg - 1) / p.rows_per_wg : 0;
+}
+__device__ inline int seq_row_blocks(const AttnParams& p, int b) {
+  return seq_row_blocks(p, p.status[b], p.num_nodes[b], p.prefix_len[b]);
+}
+
+// The work of logical block lb: (unit = sequence * Hkv + KV head, row block,
+// key range) and the key range's length.  A plan made on the host from
+// T_max gives every (unit, row block) the same key split, so with trees of
+// different sizes some row blocks hold no valid row and their workgroups
+// idle while the full ones set the time.  With p.dyn the workgroups read
+// the sequences' sizes and share out only the row blocks that hold valid
+// rows, numbered densely (unit by unit, then key range, then row block, so
+// consecutive workgroups read the same keys), with the key split as fine as
+// the grid allows (at most ls_cap, ranges of at least 4 key blocks).  Every
+// workgroup derives the same plan from the same sizes, and logical block 0
+// records the split for the merge.  Returns false when lb has no work.
+struct AttnWork {
+  int ms_i, ls_i, unit, chunk, nls;   // nls: the key split, also the partials' stride per row
+  int st, Tb, Lb;                     // the sequence's status and sizes, when the decode read them
+  bool have_seq;
+};
+__device__ inline bool decode_work(const AttnParams& p, int lb, AttnWork& wk) {
+  if (!p.dyn) {
+    wk.ms_i = lb % p.msplit;
+    const int rest = lb / p.msplit;
+    wk.ls_i = rest % p.lsplit;
+    wk.unit = rest / p.lsplit;
+    wk.chunk = p.chunk;
+    wk.nls = p.lsplit;
+    wk.have_seq = false;
+    return true;
+  }
+  const int lane = threadIdx.x & 63;
+  // Valid row blocks of the first 64 sequences, one per lane, and their
+  // inclusive scan; with more sequences, the rest add to the total in a
+  // first pass and are scanned again below.
+  const int st0 = lane < p.B ? p.status[lane] : 0;
+  const int tb0 = lane < p.B ? p.num_nodes[lane] : 0;
+  const int lb0 = lane < p.B ? p.prefix_len[lane] : 0;
+  const int rb0 = lane < p.B ? seq_row_blocks(p, st0, tb0, lb0) : 0;
+  int scan0 = rb0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(scan0, off);
+    if (lane >= off) scan0 += y;
+  }
+  int rbs = __shfl(scan0, 63);   // valid row blocks per KV head, summed over the sequences
+  for (int b0 = 64; b0 < p.B; b0 += 64) {
+    int v = b0 + lane < p.B ? seq_row_blocks(p, b0 + lane) : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    rbs += v;
+  }
+  const int R = __builtin_amdgcn_readfirstlane(rbs * p.Hkv);   // <= the grid: fits in 32 bits
+  int nls = R > 0 ? (int)gridDim.x / R : 1;
+  nls = nls < 1 ? 1 : nls;
+  nls = nls > p.ls_cap ? p.ls_cap : nls;
+  const int lmax = p.keys_max / (4 * BK);
+  nls = nls > lmax ? (lmax < 1 ? 1 : lmax) : nls;
+  wk.chunk = ((p.keys_max + nls - 1) / nls + 63) / 64 * 64;
+  wk.nls = nls;
+  if (lb == 0 && threadIdx.x == 0) *p.dyn_ls = nls;
+  if (lb >= R * nls) return false;
+  // the sequence whose items (row blocks x KV heads x key ranges) hold lb
+  const int per = p.Hkv * nls;
+  int base = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int rb = b0 == 0 ? rb0 : (b0 + lane < p.B ? seq_row_blocks(p, b0 + lane) : 0);
+    int incl = rb;
+    if (b0 == 0) {
+      incl = scan0;
+    } else {
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+    }
+    const int hi = base + incl * per, lo = hi - rb * per;
+    const uint64_t hit = __ballot(rb > 0 && lo <= lb && lb < hi);
+    if (hit) {
+      const int l = (int)__ffsll((unsigned long long)hit) - 1;
+      const int hrb = __shfl(rb, l);
+      const int r = lb - __shfl(lo, l);
+      const int kvh = r / (hrb * nls);
+      const int idx = r % (hrb * nls);
+      wk.ls_i = idx / hrb;
+      wk.ms_i = idx % hrb;
+      wk.unit = (b0 + l) * p.Hkv + kvh;
+      wk.have_seq = b0 == 0;   // lane l of the first 64 holds the sequence's own values
+      wk.st = __shfl(st0, l);
+      wk.Tb = __shfl(tb0, l);
+      wk.Lb = __shfl(lb0, l);
+      return true;
+    }
+    base += __shfl(incl, 63) * per;
+  }
+  return false;
 }
 
 // Max over the 4 lanes holding one tile column (lanes c, c+16, c+32,
@@ -161,10 +269,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem_raw + kStages * STAGE * sizeof(__bf16));
 
   const int lb = logical_block(p.remap);
-  const int ms_i = lb % p.msplit;
-  const int rest = lb / p.msplit;
-  const int ls_i = rest % p.lsplit;
-  const int unit = rest / p.lsplit;
+  AttnWork wk;
+  if (!decode_work(p, lb, wk)) return;
+  // the same in every lane: scalar registers, not vector ones held through the loop
+  const int ms_i = __builtin_amdgcn_readfirstlane(wk.ms_i);
+  const int ls_i = __builtin_amdgcn_readfirstlane(wk.ls_i);
+  const int unit = __builtin_amdgcn_readfirstlane(wk.unit);
+  wk.chunk = __builtin_amdgcn_readfirstlane(wk.chunk);
+  const int nls = __builtin_amdgcn_readfirstlane(wk.nls);
   const int b = unit / p.Hkv;
   const int kvh = unit % p.Hkv;
   const int G = p.G;
@@ -175,15 +287,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int c = lane & 15;   // column (query row) within a 16x16 tile
   const int g = lane >> 4;   // lane group
 
-  const int Tb = p.num_nodes[b];
-  const int Lb = p.prefix_len[b];
+  const bool have_seq = __builtin_amdgcn_readfirstlane(wk.have_seq ? 1 : 0) != 0;
+  const int Tb = have_seq ? __builtin_amdgcn_readfirstlane(wk.Tb) : p.num_nodes[b];
+  const int Lb = have_seq ? __builtin_amdgcn_readfirstlane(wk.Lb) : p.prefix_len[b];
+  const int st_b = have_seq ? __builtin_amdgcn_readfirstlane(wk.st) : p.status[b];
   // a sequence whose tree is invalid, or whose sizes are out of range, is
   // written as zeros
-  const bool seq_ok = p.status[b] == SV_TREE_OK && Tb >= 1 && Tb <= p.T_max && Lb >= 0 && Lb <= p.L_max;
+  const bool seq_ok = st_b == SV_TREE_OK && Tb >= 1 && Tb <= p.T_max && Lb >= 0 && Lb <= p.L_max;
   const int row0 = ms_i * p.rows_per_wg;
   const int valid_rows = seq_ok ? Tb * G : 0;
-  const int kbeg = ls_i * p.chunk;
-  const int kend = min(kbeg + p.chunk, Lb + Tb);
+  const int kbeg = ls_i * wk.chunk;
+  const int kend = min(kbeg + wk.chunk, Lb + Tb);
 
   const __bf16* qp = reinterpret_cast<const __bf16*>(p.q);
   const __bf16* kc = reinterpret_cast<const __bf16*>(p.k_cache) + ((size_t)b * p.Hkv + kvh) * p.L_max * D;
@@ -218,12 +332,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int dt = 0; dt < DT; ++dt)
           *reinterpret_cast<uint2*>(o + dt * 16 + 4 * g) = make_uint2(0u, 0u);
       } else if (rvalid[qt]) {
-        float* po = p.part_o + (orow * p.lsplit + ls_i) * D;
+        float* po = p.part_o + (orow * nls + ls_i) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
           *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
         if (g == 0) {
-          float* pm = p.part_ml + (orow * p.lsplit + ls_i) * 2;
+          float* pm = p.part_ml + (orow * nls + ls_i) * 2;
           pm[0] = -INFINITY;
           pm[1] = 0.f;
         }
@@ -527,13 +641,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         *reinterpret_cast<uint2*>(o + dt * 16 + 4 * g) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     } else if (rvalid[qt]) {
-      float* po = p.part_o + (orow * p.lsplit + ls_i) * D;
+      float* po = p.part_o + (orow * nls + ls_i) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
             make_float4(acc[qt][dt][0], acc[qt][dt][1], acc[qt][dt][2], acc[qt][dt][3]);
       if (g == 0) {
-        float* pm = p.part_ml + (orow * p.lsplit + ls_i) * 2;
+        float* pm = p.part_ml + (orow * nls + ls_i) * 2;
         pm[0] = valid[qt] ? mu[qt] * c2 : -INFINITY;   // log2 units for the merge
         pm[1] = l;
       }
@@ -654,16 +768,17 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
 #pragma unroll
   for (int k = 0; k < DPL; ++k) o[k] = 0.f;
   if (valid) {
-    const float* pm = p.part_ml + (size_t)row * p.lsplit * 2;
+    const int nls = p.dyn ? *p.dyn_ls : p.lsplit;   // also the stride of a row's partials
+    const float* pm = p.part_ml + (size_t)row * nls * 2;
     float m = -INFINITY;
-    for (int s = 0; s < p.lsplit; ++s) m = fmaxf(m, pm[2 * s]);
+    for (int s = 0; s < nls; ++s) m = fmaxf(m, pm[2 * s]);
     float l = 0.f;
-    for (int s = 0; s < p.lsplit; ++s) {
+    for (int s = 0; s < nls; ++s) {
       const float ms = pm[2 * s];
       if (ms == -INFINITY) continue;
       const float w = exp2f(ms - m);
       l += w * pm[2 * s + 1];
-      const float* po = p.part_o + ((size_t)row * p.lsplit + s) * D;
+      const float* po = p.part_o + ((size_t)row * nls + s) * D;
 #pragma unroll
       for (int k = 0; k < DPL; ++k) o[k] = fmaf(w, po[lane + 64 * k], o[k]);
     }
@@ -814,15 +929,29 @@ bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* pl) {
   }
   const long per = (keys + pl->lsplit - 1) / pl->lsplit;
   pl->chunk = (int)((per + 63) / 64 * 64);
+  // With key splits and several row blocks per (sequence, KV head), the MFMA
+  // kernel re-plans on the device from the trees' actual sizes (up to 4x this
+  // split, at most 16); trees of T_max nodes give exactly this plan.
+  // SV_ATTN_LSPLIT (a forced split) and SV_ATTN_DYN=0 keep the host's plan.
+  pl->dyn = 0;
+  pl->ls_cap = pl->lsplit;
+  const char* dyn_env = getenv("SV_ATTN_DYN");
+  if (pl->kernel == 0 && pl->lsplit > 1 && pl->msplit > 1 && !getenv("SV_ATTN_LSPLIT") &&
+      !(dyn_env && atoi(dyn_env) == 0)) {
+    pl->dyn = 1;
+    pl->ls_cap = (int)std::min(16L, 4L * pl->lsplit);
+    if (pl->ls_cap < pl->lsplit) pl->ls_cap = pl->lsplit;
+  }
   if (getenv("SV_DEBUG_PLAN"))
-    fprintf(stderr, "sv attention plan: kernel=%d nt=%d nwave=%d rows/wg=%d msplit=%d lsplit=%d chunk=%d cus=%d resident=%d\n",
-            pl->kernel, pl->nt, pl->nwave, pl->rows_per_wg, pl->msplit, pl->lsplit, pl->chunk, di.num_cu,
-            pl->kernel == 0 ? resident_groups(a->D, pl->nt, pl->nwave, smem_bytes(a->D, t->T_max)) : 0);
+    fprintf(stderr, "sv attention plan: kernel=%d nt=%d nwave=%d rows/wg=%d msplit=%d lsplit=%d chunk=%d dyn=%d cap=%d "
+            "cus=%d resident=%d\n",
+            pl->kernel, pl->nt, pl->nwave, pl->rows_per_wg, pl->msplit, pl->lsplit, pl->chunk, pl->dyn, pl->ls_cap,
+            di.num_cu, pl->kernel == 0 ? resident_groups(a->D, pl->nt, pl->nwave, smem_bytes(a->D, t->T_max)) : 0);
   pl->ws_bytes = 0;
   if (pl->lsplit > 1) {
-    const size_t rows = (size_t)t->B * t->T_max * a->Hq * pl->lsplit;
+    const size_t rows = (size_t)t->B * t->T_max * a->Hq * pl->ls_cap;
     pl->ws_bytes = align_up(rows * a->D * sizeof(float), kWsAlign) +
-                   align_up(rows * 2 * sizeof(float), kWsAlign);
+                   align_up(rows * 2 * sizeof(float), kWsAlign) + (pl->dyn ? kWsAlign : 0);
   }
   return true;
 }
@@ -867,13 +996,20 @@ sv_status launch_attention(const sv_tree* t, const uint64_t* anc, const int32_t*
   prm.msplit = pl.msplit;
   prm.lsplit = pl.lsplit;
   prm.chunk = pl.chunk;
+  prm.lstride = pl.ls_cap;
+  prm.dyn = pl.dyn;
+  prm.ls_cap = pl.ls_cap;
+  prm.keys_max = a->L_max + t->T_max;
   const double scale = a->scale > 0.f ? (double)a->scale : 1.0 / sqrt((double)a->D);
   prm.scale_log2 = (float)(scale * 1.4426950408889634);
   prm.raise_raw = 8.f / prm.scale_log2;
   if (pl.lsplit > 1) {
-    const size_t rows = (size_t)t->B * t->T_max * a->Hq * pl.lsplit;
+    const size_t rows = (size_t)t->B * t->T_max * a->Hq * pl.ls_cap;
+    const size_t o_bytes = align_up(rows * a->D * sizeof(float), kWsAlign);
+    const size_t ml_bytes = align_up(rows * 2 * sizeof(float), kWsAlign);
     prm.part_o = reinterpret_cast<float*>(ws);
-    prm.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * a->D * sizeof(float), kWsAlign));
+    prm.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+    if (pl.dyn) prm.dyn_ls = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + o_bytes + ml_bytes);
   }
   hipError_t e = hipSuccess;
   if (pl.kernel == 1) {

@@ -72,6 +72,8 @@ struct AttnPlan {
   int msplit;       // workgroups along the query rows of one (sequence, KV head)
   int lsplit;       // workgroups along the key axis
   int chunk;        // keys per L split (multiple of the key block)
+  int dyn;          // MFMA kernel with lsplit > 1: the split follows the trees' actual sizes on the device
+  int ls_cap;       // largest split the device may choose (partials per row in the workspace)
   size_t ws_bytes;  // partial results when lsplit > 1
 };
 bool plan_attention(const sv_tree* t, const sv_attn_args* a, AttnPlan* p);

@@ -2,7 +2,8 @@
 
 Small cases are compared element by element (several key blocks, ragged
 prefixes including 0, ragged trees, T_b = 1, every instantiated kernel shape,
-forced key splits, fp32 and bf16).  The five workload shapes run at full size
+forced key splits, the plan made on the device from the trees' actual sizes,
+fp32 and bf16).  The five workload shapes run at full size
 in the launch configuration the benchmark uses and are compared on every
 output element.  Peaked inputs (queries and keys with std 2, 3, 4, i.e. score
 spreads of 4 to 16 in natural units, and one planted dominant key per row on
@@ -123,6 +124,30 @@ def test_attention_invalid_sequences_zero():
     got = dev.attn_result()
     assert np.abs(got[0]).sum() > 0
     assert not got[1].any() and not got[2].any()
+
+
+@pytest.mark.parametrize("dyn", ["1", "0"])
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_sizes_driven_plan(D, dyn, capfd):
+    """With key splits and several row blocks per (sequence, KV head), the
+    kernel shares out only the row blocks that hold valid rows and picks the
+    key split from the trees' actual sizes.  80 sequences (more than one wave
+    of 64 counts them), trees of 1 to 40 nodes, prefixes including 0, and two
+    invalid sequences (no row blocks); SV_ATTN_DYN=0 keeps the host's plan."""
+    need_gpu()
+    rng = np.random.default_rng(11)
+    B = 80
+    prefix = rng.integers(0, 700, size=B).tolist()
+    prefix[3] = 0
+    spec = _spec(B=B, Hq=8, Hkv=1, D=D, prefix_len=prefix, tree=("dynamic", 1, 5, 1, 6, 1, 40), T_max=40)
+    inst = make_instance(spec, 12, with_accept=False)
+    big = [b for b in range(B) if inst.num_nodes[b] >= 3]
+    inst.parent[big[0], 2] = 7          # parent not before its child
+    inst.parent[big[1], 1] = -1         # a second root
+    _run(inst, f"sizes-driven plan D={D} dyn={dyn}", env={"SV_ATTN_DYN": dyn, "SV_DEBUG_PLAN": "1"})
+    plan = capfd.readouterr().err
+    assert f"dyn={dyn}" in plan, plan
+    assert "msplit=1 " not in plan and "lsplit=1 " not in plan, plan
 
 
 @pytest.mark.parametrize("cfg", [c["name"] for c in CONFIGS])
