@@ -51,9 +51,9 @@ struct AttnParams {
   const int32_t* status;
   const uint64_t* anc;
   void* out;
-  float* part_o;   // [B][T_max][Hq][n][D], n = the key split in use (room for lstride)
-  float* part_ml;  // [B][T_max][Hq][n][2]
-  int32_t* dyn_ls; // the key split a sizes-driven plan chose (read by the merge)
+  float* part_o;   // [B][T_max][Hq][lstride][D]: the key ranges' partials, first n in use
+  float* part_ml;  // [B][T_max][Hq][lstride][2]
+  int32_t* dyn_ls; // the key split n a sizes-driven plan chose (read by the merge)
   int B, T_max, Hq, Hkv, G, L_max, W;
   int rows_per_wg, msplit, lsplit, chunk;
   int lstride;     // partials per row the workspace holds: lsplit, or ls_cap with dyn
@@ -95,7 +95,7 @@ __device__ inline int seq_row_blocks(const AttnParams& p, int b) {
 // workgroup derives the same plan from the same sizes, and logical block 0
 // records the split for the merge.  Returns false when lb has no work.
 struct AttnWork {
-  int ms_i, ls_i, unit, chunk, nls;   // nls: the key split, also the partials' stride per row
+  int ms_i, ls_i, unit, chunk, nls;   // nls: the key split
   int st, Tb, Lb;                     // the sequence's status and sizes, when the decode read them
   bool have_seq;
 };
@@ -332,12 +332,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int dt = 0; dt < DT; ++dt)
           *reinterpret_cast<uint2*>(o + dt * 16 + 4 * g) = make_uint2(0u, 0u);
       } else if (rvalid[qt]) {
-        float* po = p.part_o + (orow * nls + ls_i) * D;
+        float* po = p.part_o + (orow * p.lstride + ls_i) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
           *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
         if (g == 0) {
-          float* pm = p.part_ml + (orow * nls + ls_i) * 2;
+          float* pm = p.part_ml + (orow * p.lstride + ls_i) * 2;
           pm[0] = -INFINITY;
           pm[1] = 0.f;
         }
@@ -641,13 +641,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         *reinterpret_cast<uint2*>(o + dt * 16 + 4 * g) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     } else if (rvalid[qt]) {
-      float* po = p.part_o + (orow * nls + ls_i) * D;
+      float* po = p.part_o + (orow * p.lstride + ls_i) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
             make_float4(acc[qt][dt][0], acc[qt][dt][1], acc[qt][dt][2], acc[qt][dt][3]);
       if (g == 0) {
-        float* pm = p.part_ml + (orow * nls + ls_i) * 2;
+        float* pm = p.part_ml + (orow * p.lstride + ls_i) * 2;
         pm[0] = valid[qt] ? mu[qt] * c2 : -INFINITY;   // log2 units for the merge
         pm[1] = l;
       }
@@ -752,54 +752,97 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnParams p) {
 
 // ----------------------------------------------------------------------------
 // Merge of key-range partials: m = max m_s, O = sum 2^(m_s - m) O_s / sum
-// 2^(m_s - m) l_s.  One wave per output row; invalid rows are zeroed.
+// 2^(m_s - m) l_s.  One thread per (row, 4 output dims); invalid rows are
+// zeroed.  The merge is bound by memory latency, not bytes: a thread issues
+// the sequence's sizes, the split in use and the offsets m_s of every range
+// the workspace holds in one round trip (the ranges past the split are
+// ignored), then (l_s, O_s) of 4 ranges per further one.  Few
+// registers keep all rows of the workloads resident at once.
 // ----------------------------------------------------------------------------
 template <bool BF16, int D>
-__global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
-  const int lane = threadIdx.x;
-  const int row = blockIdx.x;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_attn_combine(AttnParams p) {
+  constexpr int LPR = D / 4;            // threads per row
+  constexpr int RPG = 256 / LPR;        // rows per workgroup
+  constexpr int NM = 16;                // offsets loaded in the first round trip
+  constexpr int NB = 4;                 // ranges per batch of O loads
+  const int row = blockIdx.x * RPG + threadIdx.x / LPR;
+  const int c4 = threadIdx.x % LPR;
+  if (row >= p.B * p.T_max * p.Hq) return;
   const int t = (row / p.Hq) % p.T_max;
   const int b = row / (p.Hq * p.T_max);
+  const float* pm = p.part_ml + (size_t)row * p.lstride * 2;
+  const float4* po = reinterpret_cast<const float4*>(p.part_o) + (size_t)row * p.lstride * LPR + c4;
+  // first round trip: everything that does not depend on another load
   const int Tb = p.num_nodes[b];
   const int Lb = p.prefix_len[b];
-  const bool valid = p.status[b] == SV_TREE_OK && t < Tb && Tb <= p.T_max && Lb >= 0 && Lb <= p.L_max;
-  constexpr int DPL = D / 64;
-  float o[DPL];
+  const int st = p.status[b];
+  const int nls = p.dyn ? *p.dyn_ls : p.lsplit;
+  float mv[NM];
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+  for (int s = 0; s < NM; ++s)
+    if (s < p.lstride) mv[s] = pm[2 * s];
+  const bool valid = st == SV_TREE_OK && t < Tb && Tb <= p.T_max && Lb >= 0 && Lb <= p.L_max;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   if (valid) {
-    const int nls = p.dyn ? *p.dyn_ls : p.lsplit;   // also the stride of a row's partials
-    const float* pm = p.part_ml + (size_t)row * nls * 2;
-    float m = -INFINITY;
-    for (int s = 0; s < nls; ++s) m = fmaxf(m, pm[2 * s]);
-    float l = 0.f;
-    for (int s = 0; s < nls; ++s) {
-      const float ms = pm[2 * s];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - m);
-      l += w * pm[2 * s + 1];
-      const float* po = p.part_o + ((size_t)row * nls + s) * D;
+    float m = -INFINITY, l = 0.f;
+    if (nls <= NM && p.lstride <= NM) {
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) o[k] = fmaf(w, po[lane + 64 * k], o[k]);
+      for (int s = 0; s < NM; ++s)
+        if (s < nls) m = fmaxf(m, mv[s]);
+#pragma unroll
+      for (int s = 0; s < NM; ++s) mv[s] = (s < nls && mv[s] != -INFINITY) ? exp2f(mv[s] - m) : 0.f;
+#pragma unroll
+      for (int s0 = 0; s0 < NM; s0 += NB) {
+        if (s0 >= nls) break;
+        float ls[NB];
+        float4 v[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (mv[s0 + j] != 0.f) {
+            ls[j] = pm[2 * (s0 + j) + 1];
+            v[j] = po[(s0 + j) * LPR];
+          }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const float w = mv[s0 + j];
+          if (w != 0.f) {
+            l = fmaf(w, ls[j], l);
+            o.x = fmaf(w, v[j].x, o.x);
+            o.y = fmaf(w, v[j].y, o.y);
+            o.z = fmaf(w, v[j].z, o.z);
+            o.w = fmaf(w, v[j].w, o.w);
+          }
+        }
+      }
+    } else {
+      for (int s = 0; s < nls; ++s) m = fmaxf(m, pm[2 * s]);
+      for (int s = 0; s < nls; ++s) {
+        const float ms = pm[2 * s];
+        if (ms == -INFINITY) continue;
+        const float w = exp2f(ms - m);
+        const float4 v = po[s * LPR];
+        l = fmaf(w, pm[2 * s + 1], l);
+        o.x = fmaf(w, v.x, o.x);
+        o.y = fmaf(w, v.y, o.y);
+        o.z = fmaf(w, v.z, o.z);
+        o.w = fmaf(w, v.w, o.w);
+      }
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] *= inv;
+    o.x *= inv;
+    o.y *= inv;
+    o.z *= inv;
+    o.w *= inv;
   }
   if (BF16) {
-    __bf16* out = reinterpret_cast<__bf16*>(p.out) + (size_t)row * D;
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) out[lane + 64 * k] = (__bf16)o[k];
+    __bf16* out = reinterpret_cast<__bf16*>(p.out) + (size_t)row * D + 4 * c4;
+    *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
   } else {
-    float* out = reinterpret_cast<float*>(p.out) + (size_t)row * D;
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) out[lane + 64 * k] = o[k];
+    float* out = reinterpret_cast<float*>(p.out) + (size_t)row * D + 4 * c4;
+    *reinterpret_cast<float4*>(out) = o;
   }
 }
 
-// ----------------------------------------------------------------------------
-// host side: launch planning
-// ----------------------------------------------------------------------------
 const void* variant_kernel(int D, int nt, int nw) {
   switch (D * 100 + nt * 10 + nw) {
     case 12834: return (const void*)k_attn_bf16<128, 3, 4>;
@@ -1041,12 +1084,14 @@ sv_status launch_attention(const sv_tree* t, const uint64_t* anc, const int32_t*
   }
   if (pl.lsplit > 1) {
     const int rows = t->B * t->T_max * a->Hq;
+    const int rpg = 256 / (a->D / 4);   // rows per merge workgroup
+    const dim3 grid((rows + rpg - 1) / rpg);
     if (a->dtype == SV_BF16) {
-      if (a->D == 64) hipLaunchKernelGGL((k_attn_combine<true, 64>), dim3(rows), dim3(64), 0, s, prm);
-      else hipLaunchKernelGGL((k_attn_combine<true, 128>), dim3(rows), dim3(64), 0, s, prm);
+      if (a->D == 64) hipLaunchKernelGGL((k_attn_combine<true, 64>), grid, dim3(256), 0, s, prm);
+      else hipLaunchKernelGGL((k_attn_combine<true, 128>), grid, dim3(256), 0, s, prm);
     } else {
-      if (a->D == 64) hipLaunchKernelGGL((k_attn_combine<false, 64>), dim3(rows), dim3(64), 0, s, prm);
-      else hipLaunchKernelGGL((k_attn_combine<false, 128>), dim3(rows), dim3(64), 0, s, prm);
+      if (a->D == 64) hipLaunchKernelGGL((k_attn_combine<false, 64>), grid, dim3(256), 0, s, prm);
+      else hipLaunchKernelGGL((k_attn_combine<false, 128>), grid, dim3(256), 0, s, prm);
     }
     e = hipGetLastError();
     if (e != hipSuccess) {
