@@ -101,6 +101,17 @@ def test_attention_key_splits(lsplit, dtype):
     _run(inst, f"lsplit={lsplit} {dtype}", env={"SV_ATTN_LSPLIT": str(lsplit)})
 
 
+@pytest.mark.parametrize("lsplit", [17, 20])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_many_key_splits(lsplit, dtype):
+    """More key ranges than the merge loads in its first round trip (16):
+    the merge's loop path, with ranges that are empty for the short prefix."""
+    need_gpu()
+    spec = _spec(B=2, Hq=8, Hkv=2, dtype=dtype, prefix_len=[3000, 45], tree=("widths", [3, 3, 3]))
+    inst = make_instance(spec, 5, with_accept=False)
+    _run(inst, f"lsplit={lsplit} {dtype}", env={"SV_ATTN_LSPLIT": str(lsplit)})
+
+
 @pytest.mark.parametrize("lsplit", ["1", "3"])
 @pytest.mark.parametrize("D", [128, 64])
 def test_attention_odd_kv_heads(D, lsplit):
