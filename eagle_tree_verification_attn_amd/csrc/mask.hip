@@ -26,12 +26,14 @@ __global__ __launch_bounds__(256) void k_tree_mask_build(const int32_t* __restri
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   for (int i = b * 256 + tid; i < n_zero; i += gridDim.x * 256) zero_words[i] = 0ull;
+  // the node count and this thread's parent in one memory round trip (the
+  // parent array is [B][T_max], so the load is in bounds whatever the count)
   const int Tb = num_nodes[b];
+  const int p = tid < T_max ? parent[(size_t)b * T_max + tid] : -1;
   const bool count_ok = Tb >= 1 && Tb <= T_max;
   if (tid == 0) flags = 0;
   __syncthreads();
   if (count_ok && tid < Tb) {
-    const int p = parent[(size_t)b * T_max + tid];
     par[tid] = p;
     if (tid == 0) {
       if (p != -1) atomicOr(&flags, 1);
