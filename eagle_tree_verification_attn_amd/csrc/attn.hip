@@ -739,13 +739,13 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnParams p) {
     for (int k = 0; k < DPL; ++k)
       if (lane + 64 * k < D) out[lane + 64 * k] = o[k] * inv;
   } else if (valid) {
-    float* po = p.part_o + ((size_t)row * p.lsplit + ls_i) * D;
+    float* po = p.part_o + ((size_t)row * p.lstride + ls_i) * D;
 #pragma unroll
     for (int k = 0; k < DPL; ++k)
       if (lane + 64 * k < D) po[lane + 64 * k] = o[k];
     if (lane == 0) {
-      p.part_ml[((size_t)row * p.lsplit + ls_i) * 2] = m_run;
-      p.part_ml[((size_t)row * p.lsplit + ls_i) * 2 + 1] = l_run;
+      p.part_ml[((size_t)row * p.lstride + ls_i) * 2] = m_run;
+      p.part_ml[((size_t)row * p.lstride + ls_i) * 2 + 1] = l_run;
     }
   }
 }
