@@ -106,10 +106,12 @@ def attn_build_hash():
     return h.hexdigest()
 
 
-def counters_traffic():
+def counters_traffic(workload):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source and flags; else None."""
-    if not os.path.exists(COUNTERS):
+    summary, if it covers this workload (the counters are taken on the
+    default one) and was taken on the current kernel source and flags; else
+    None."""
+    if workload != WORKLOAD or not os.path.exists(COUNTERS):
         return None
     try:
         info = json.load(open(COUNTERS))
@@ -166,6 +168,21 @@ def summarize_counters(fetch_csv, write_csv):
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
+
+
+def tree_shape(inst):
+    """Drafted nodes (root excluded) and depth of the sequences' trees: one
+    number when every sequence has the same, else one per sequence."""
+    nodes, depths = [], []
+    for b in range(inst.B):
+        n = int(inst.num_nodes[b])
+        d = [0] * n
+        for i in range(1, n):
+            d[i] = d[int(inst.parent[b][i])] + 1
+        nodes.append(n - 1)
+        depths.append(max(d))
+    one = lambda xs: xs[0] if len(set(xs)) == 1 else xs
+    return one(nodes), one(depths)
 
 
 def step_distribution(devs, k, stream):
@@ -481,7 +498,8 @@ def main():
     # between the two, so every step's inputs were last touched two steps and
     # 2.7 GB of traffic earlier, past the 256 MB Infinity Cache (cold inputs,
     # still resident in HBM).
-    other = DeviceProblem(make_instance(cfg, 1), device="cuda:0")
+    inst1 = make_instance(cfg, 1)
+    other = DeviceProblem(inst1, device="cuda:0")
     devs = (dev, other)
     pw_ms, pw_steps = prewarm(devs, args.prewarm_seconds)
     print(f"bench: pre-warm {pw_steps} steps in {pw_ms:.0f} ms", file=sys.stderr, flush=True)
@@ -509,6 +527,7 @@ def main():
     n = max(200, args.steps)   # ~0.12 s: enough launches for a stable mean
     in_step = in_step_times(devs, n, stream)
     warm_ms = back_to_back((dev,), args.steps, stream)
+    res1 = other.accept_results()
     del other, devs
     torch.cuda.empty_cache()
 
@@ -525,16 +544,20 @@ def main():
     rates = stream_rates(stream)
     for d in (e2, head):
         d["frac_of_measured_read"] = round(d["GB_s"] / rates["read_only_GB_s"], 4)
-    flops, attn_bytes = algorithmic_work(inst)
+    # the in-step means alternate over the two input sets, so their work is
+    # the mean of the two sets' (the same when both sets' trees have one
+    # shape, as in the default workload; not with trees of random size)
+    w0, w1 = algorithmic_work(inst), algorithmic_work(inst1)
+    flops, attn_bytes = (w0[0] + w1[0]) / 2, (w0[1] + w1[1]) / 2
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
-    acc_bytes = accept_bytes(inst, res)
+    acc_bytes = (accept_bytes(inst, res) + accept_bytes(inst1, res1)) / 2
     acc_gbs = acc_bytes / (acc_ms * 1e-3) / 1e9
     sz_logit = 2 if inst.logit_dtype == "bf16" else 4
-    every_row_bytes = float(sz_logit * inst.V * int(inst.num_nodes.sum()))
+    every_row_bytes = float(sz_logit * inst.V * (int(inst.num_nodes.sum()) + int(inst1.num_nodes.sum())) / 2)
     every_row_ms = every_row_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
-    traffic = counters_traffic()
+    traffic = counters_traffic(cfg["name"])
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": "k_attn_bf16 (sv_tree_attn)",
@@ -548,6 +571,10 @@ def main():
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inst, args.cpu_seconds)
 
+    # the trees of both input sets (one entry when they have the same shape)
+    shapes = [tree_shape(inst), tree_shape(inst1)]
+    tree_nodes = shapes[0][0] if shapes[0] == shapes[1] else [sh[0] for sh in shapes]
+    tree_depth = shapes[0][1] if shapes[0] == shapes[1] else [sh[1] for sh in shapes]
     out = {
         "metric": METRIC,
         "value": round(1000.0 / ms_step, 2),
@@ -562,8 +589,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg["name"], "B": cfg["B"], "Hq": cfg["Hq"], "Hkv": cfg["Hkv"],
-                   "D": cfg["D"], "prefix_len": cfg["prefix_len"], "tree_nodes": int(inst.num_nodes[0]) - 1,
-                   "depth": 6, "V": cfg["V"], "temperature": cfg["tau"], "parallelism": "single GPU"},
+                   "D": cfg["D"], "prefix_len": cfg["prefix_len"], "tree_nodes": tree_nodes,
+                   "depth": tree_depth, "V": cfg["V"], "temperature": cfg["tau"], "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_ms": {"tree_mask_build": round(mask_ms, 5), "tree_attn": round(attn_ms, 5),
@@ -591,8 +618,9 @@ def main():
                                               "every_row_once_roofline_ms": round(every_row_ms, 5),
                                               "walk_ms_vs_that_roofline": round(acc_ms / every_row_ms, 4)},
                          "measured_stream": rates},
-        "emitted_tokens_per_seq": round(float(np.mean(res["out_count"])), 3),
-        "vocab_passes_per_seq": round(float(np.mean(res["out_passes"])), 3),
+        # over both input sets, like the timed steps
+        "emitted_tokens_per_seq": round(float(np.mean(np.concatenate([res["out_count"], res1["out_count"]]))), 3),
+        "vocab_passes_per_seq": round(float(np.mean(np.concatenate([res["out_passes"], res1["out_passes"]]))), 3),
     }
     print(json.dumps(out))
 
