@@ -1,7 +1,9 @@
-"""The benchmark's command line, without a GPU: more than one GPU is refused
-with a message and exit status 2 (this build measures one GPU), and the
-counter summary mode turns two rocprofv3 counter files into the calibrated
-per-launch HBM figure."""
+"""The benchmark's command line and result-line helpers, without a GPU: more
+than one GPU is refused with a message and exit status 2 (this build measures
+one GPU); the counter summary mode turns two rocprofv3 counter files into the
+calibrated per-launch HBM figure, which the result line carries only for the
+workload and kernel build it was taken on; the tree shapes it reports come
+from the parent arrays."""
 import csv
 import json
 import os
@@ -60,3 +62,31 @@ def test_counter_hash_tracks_flags_not_location(monkeypatch):
     assert bench.attn_build_hash() == h0
     monkeypatch.setattr(B, "FILE_FLAGS", {"attn.hip": B.FILE_FLAGS["attn.hip"] + ["-O2"]})
     assert bench.attn_build_hash() != h0
+
+
+def test_counter_traffic_only_for_its_workload(tmp_path, monkeypatch):
+    """The committed counters are taken on the default workload: the result
+    line carries their HBM bytes for that workload only (null for any other
+    --config), and only while the kernel's source and flags are unchanged."""
+    import bench
+    out = tmp_path / "counters.json"
+    out.write_text(json.dumps({"attn_build_sha256": bench.attn_build_hash(), "hbm_bytes_per_launch": 123456}))
+    monkeypatch.setattr(bench, "COUNTERS", str(out))
+    assert bench.counters_traffic(bench.WORKLOAD) == 123456.0
+    assert bench.counters_traffic("long_ctx_dynamic") is None
+    out.write_text(json.dumps({"attn_build_sha256": "0" * 64, "hbm_bytes_per_launch": 123456}))
+    assert bench.counters_traffic(bench.WORKLOAD) is None
+
+
+def test_tree_shape_of_the_result_line():
+    """Drafted nodes (root excluded) and depth per sequence, from the parent
+    arrays: one number when all sequences agree, else one per sequence."""
+    import types
+    import numpy as np
+    import bench
+    chain = [-1, 0, 1, 2, -1]          # root, then a chain of 3 (depth 3); one unused slot
+    star = [-1, 0, 0, 0, 0]            # root with 4 children (depth 1)
+    inst = types.SimpleNamespace(B=2, num_nodes=np.array([4, 5]), parent=np.array([chain, star]))
+    assert bench.tree_shape(inst) == ([3, 4], [3, 1])
+    same = types.SimpleNamespace(B=2, num_nodes=np.array([5, 5]), parent=np.array([star, star]))
+    assert bench.tree_shape(same) == (4, 1)
