@@ -443,6 +443,9 @@ def main():
     ap.add_argument("--prewarm-seconds", type=float, default=2.0,
                     help="untimed steps for this long before the warm-up steps (clock and power settle)")
     ap.add_argument("--config", default=WORKLOAD)
+    ap.add_argument("--kv-shards", type=int, default=1,
+                    help="time one GPU's share of the workload when the target is tensor-parallel over "
+                         "this many GPUs (attention sharded by KV head: Hq / n and Hkv / n heads)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels-only", action="store_true",
@@ -467,11 +470,11 @@ def main():
     import torch
     import eagle_tree_verification_attn_amd as sv
     from eagle_tree_verification_attn_amd.problem import DeviceProblem
-    from synth import config_by_name, make_instance
+    from synth import config_by_name, kv_head_shard, make_instance
 
     sv.lib()   # fails loudly if the HIP library is missing
     torch.cuda.set_device(0)
-    cfg = config_by_name(args.config)
+    cfg = kv_head_shard(config_by_name(args.config), args.kv_shards)
     t0 = time.perf_counter()
     inst = make_instance(cfg, 0)
     gen_s = time.perf_counter() - t0
@@ -590,7 +593,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg["name"], "B": cfg["B"], "Hq": cfg["Hq"], "Hkv": cfg["Hkv"],
                    "D": cfg["D"], "prefix_len": cfg["prefix_len"], "tree_nodes": tree_nodes,
-                   "depth": tree_depth, "V": cfg["V"], "temperature": cfg["tau"], "parallelism": "single GPU"},
+                   "depth": tree_depth, "V": cfg["V"], "temperature": cfg["tau"],
+                   "parallelism": ("single GPU" if args.kv_shards == 1 else
+                                   f"one GPU's share of a {args.kv_shards}-way KV-head split (accept not split)")},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_ms": {"tree_mask_build": round(mask_ms, 5), "tree_attn": round(attn_ms, 5),

@@ -7,10 +7,10 @@ verification arithmetic itself: no tree mask, no attention, no target softmax,
 no accept/reject rule.  The draft distribution q and the draft tokens are the
 drafter's outputs, so producing them belongs here (a synthetic drafter).
 """
-from .configs import CONFIGS, config_by_name, small_spec
+from .configs import CONFIGS, config_by_name, kv_head_shard, small_spec
 from .gen import (Instance, make_instance, bf16_bits_from_f32, f32_from_bf16_bits,
                   tree_from_widths, random_tree_widths, make_draft_rows, make_head_inputs)
 
-__all__ = ["CONFIGS", "config_by_name", "small_spec", "Instance", "make_instance",
+__all__ = ["CONFIGS", "config_by_name", "kv_head_shard", "small_spec", "Instance", "make_instance",
            "bf16_bits_from_f32", "f32_from_bf16_bits", "tree_from_widths",
            "random_tree_widths", "make_draft_rows", "make_head_inputs"]

@@ -48,3 +48,19 @@ def small_spec(base, **over):
     s = dict(config_by_name(base) if isinstance(base, (str, int)) else base)
     s.update(over)
     return s
+
+
+def kv_head_shard(base, n):
+    """One GPU's share of a workload whose target model is tensor-parallel over
+    n GPUs.  Attention then shards by KV head: each GPU holds Hkv / n KV heads
+    and their Hq / n query heads, with every sequence, prefix and tree
+    unchanged.  The inputs are drawn for that shape from the workload's own
+    seeds."""
+    s = dict(config_by_name(base) if isinstance(base, (str, int)) else base)
+    if n < 1 or s["Hkv"] % n:
+        raise ValueError(f"{s['name']}: {s['Hkv']} KV heads do not split {n} ways")
+    if n > 1:
+        s["Hq"] //= n
+        s["Hkv"] //= n
+        s["name"] = f"{s['name']}_kvshard{n}"
+    return s

@@ -90,3 +90,20 @@ def test_tree_shape_of_the_result_line():
     assert bench.tree_shape(inst) == ([3, 4], [3, 1])
     same = types.SimpleNamespace(B=2, num_nodes=np.array([5, 5]), parent=np.array([star, star]))
     assert bench.tree_shape(same) == (4, 1)
+
+
+def test_kv_head_shard_is_one_gpus_share():
+    """`bench.py --kv-shards n` times one GPU's share under an n-way KV-head
+    split: Hq / n and Hkv / n heads, everything else as in the workload; a
+    split that does not divide the KV heads is refused."""
+    import pytest
+    from synth import config_by_name, kv_head_shard
+    full = config_by_name("tree64_llama70b_b32")
+    s = kv_head_shard("tree64_llama70b_b32", 8)
+    assert (s["Hq"], s["Hkv"]) == (8, 1) and s["Hq"] // s["Hkv"] == full["Hq"] // full["Hkv"]
+    assert {k: v for k, v in s.items() if k not in ("Hq", "Hkv", "name")} == \
+        {k: v for k, v in full.items() if k not in ("Hq", "Hkv", "name")}
+    assert s["name"] != full["name"]
+    assert kv_head_shard(full, 1) == full
+    with pytest.raises(ValueError):
+        kv_head_shard(full, 3)

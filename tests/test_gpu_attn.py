@@ -5,7 +5,8 @@ prefixes including 0, ragged trees, T_b = 1, every instantiated kernel shape,
 forced key splits, the plan made on the device from the trees' actual sizes,
 fp32 and bf16).  The five workload shapes run at full size
 in the launch configuration the benchmark uses and are compared on every
-output element.  Peaked inputs (queries and keys with std 2, 3, 4, i.e. score
+output element, and so is one GPU's share of the 70B-shaped batch under a 2-
+and 8-way KV-head split.  Peaked inputs (queries and keys with std 2, 3, 4, i.e. score
 spreads of 4 to 16 in natural units, and one planted dominant key per row on
 the row's own tree node, its parent or a prefix key) cover the regime of a
 trained target's forward pass, at a short-prefix shape and at the full
@@ -18,7 +19,7 @@ import pytest
 
 import oracle
 from gpu_util import check_attention, need_gpu, say, sv_problem
-from synth import CONFIGS, make_instance
+from synth import CONFIGS, kv_head_shard, make_instance
 
 pytestmark = pytest.mark.gpu
 
@@ -168,6 +169,22 @@ def test_attention_full_workloads(cfg):
     spec = dict(next(c for c in CONFIGS if c["name"] == cfg))
     inst = make_instance(spec, 0, with_accept=False)
     _run(inst, f"full {cfg}")
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_attention_kv_head_shard(n, capfd):
+    """One GPU's share of the Llama-3-70B-shaped batch when the target is
+    tensor-parallel over n GPUs: 32 sequences, 64/n query and 8/n KV heads,
+    prefix 8192, 65 tree positions.  With one KV head (n = 8) there are only
+    32 (sequence, KV head) units, and the plan splits the keys to fill the
+    GPU; every output row is compared."""
+    need_gpu()
+    spec = kv_head_shard("tree64_llama70b_b32", n)
+    inst = make_instance(spec, 0, with_accept=False)
+    _run(inst, f"kv-head shard 1/{n}", env={"SV_DEBUG_PLAN": "1"})
+    plan = capfd.readouterr().err
+    if n == 8:
+        assert "lsplit=1 " not in plan, plan
 
 
 @pytest.mark.parametrize("plant", [None, 6.0])
