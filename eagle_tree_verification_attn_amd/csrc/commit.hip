@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(CommitParams p) {
     if (bad_s) {
       go = false;
       new_status = SV_TREE_E_PATH;
-    } else if (L < 0 || L + c > p.L_max) {
+    } else if (L < 0 || (long)L + c > p.L_max) {
       go = false;
       new_status = SV_TREE_E_CACHE;
     }

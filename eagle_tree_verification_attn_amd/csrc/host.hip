@@ -62,6 +62,12 @@ sv_status check_attn(const sv_tree* t, const sv_attn_args* a) {
   if (a->D != 64 && a->D != 128) { set_error("head dim %d (supported: 64, 128)", a->D); return SV_E_UNSUPPORTED; }
   if (a->dtype != SV_F32 && a->dtype != SV_BF16) { set_error("attention dtype %d", a->dtype); return SV_E_DTYPE; }
   if ((long)t->B * t->T_max * a->Hq > 0x7FFFFFFFL) { set_error("B*T_max*Hq too large"); return SV_E_UNSUPPORTED; }
+  // the kernels address a (sequence, KV head)'s keys with 32-bit element
+  // offsets: (L_max + T_max) * D must stay below 2^31
+  if (((long)a->L_max + kMaxT) * a->D > 0x7FFFFFFFL) {
+    set_error("L_max = %d too large for D = %d (need (L_max + %d) * D < 2^31)", a->L_max, a->D, kMaxT);
+    return SV_E_UNSUPPORTED;
+  }
   if (t->B > 0) {
     if (!a->q || !a->k_new || !a->v_new || !a->out || !a->prefix_len) {
       set_error("attention q/k_new/v_new/out/prefix_len is NULL");

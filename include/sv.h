@@ -99,7 +99,8 @@ typedef struct {
 /* Tree attention inputs (post-RoPE projections of one layer). */
 typedef struct {
   int32_t Hq, Hkv, D;       /* query heads, KV heads (Hq % Hkv == 0), head dim          */
-  int32_t L_max;            /* capacity of the cache's length axis (>= max L_b)         */
+  int32_t L_max;            /* capacity of the cache's length axis (>= max L_b);        */
+                            /* (L_max + 256) * D < 2^31, else SV_E_UNSUPPORTED          */
   int32_t dtype;            /* SV_F32 or SV_BF16, for q, k_new, v_new, caches and out   */
   float scale;              /* score scale; <= 0 means 1/sqrt(D)                        */
   const void* q;            /* [B][T_max][Hq][D]  queries of the tree positions         */

@@ -84,6 +84,11 @@ def test_host_validation_rejects_before_launch():
     assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(dtype=7)), fake, 1 << 30, null) == sv.SV_E_DTYPE
     assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(q=None)), fake, 1 << 30, null) == sv.SV_E_NULL
     assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(q=0x10008)), fake, 1 << 30, null) == sv.SV_E_UNSUPPORTED
+    # 32-bit key offsets: (L_max + 256) * D must stay below 2^31
+    big = (1 << 31) // 64 - 256
+    assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(L_max=big)), fake, 1 << 30, null) == sv.SV_E_UNSUPPORTED
+    assert b"too large for D" in L.sv_last_error()
+    assert L.sv_tree_attn(t, fake, fake, ctypes.byref(_attn(L_max=big - 1, q=None)), fake, 1 << 30, null) == sv.SV_E_NULL
     assert L.sv_spec_accept(t, fake, ctypes.byref(_acc(V=0)), fake, 1 << 30, null) == sv.SV_E_SHAPE
     assert L.sv_spec_accept(t, fake, ctypes.byref(_acc(logit_dtype=5)), fake, 1 << 30, null) == sv.SV_E_DTYPE
     assert L.sv_spec_accept(t, fake, ctypes.byref(_acc(sibling_mode=2)), fake, 1 << 30, null) == sv.SV_E_SHAPE
