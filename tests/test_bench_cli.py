@@ -3,12 +3,16 @@ than one GPU is refused with a message and exit status 2 (this build measures
 one GPU); the counter summary mode turns two rocprofv3 counter files into the
 calibrated per-launch HBM figure, which the result line carries only for the
 workload and kernel build it was taken on; the tree shapes it reports come
-from the parent arrays."""
+from the parent arrays; the roofline's algorithmic flops and bytes match the
+headline workload's closed form and a pair-by-pair count of visible keys."""
 import csv
 import json
 import os
 import subprocess
 import sys
+import types
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -107,3 +111,58 @@ def test_kv_head_shard_is_one_gpus_share():
     assert kv_head_shard(full, 1) == full
     with pytest.raises(ValueError):
         kv_head_shard(full, 3)
+
+
+def _tree_from_widths(widths):
+    """Parent array of a tree numbered by depth: each node's parent is the
+    first node of the previous depth (depth sums do not depend on which)."""
+    parent = [-1]
+    first_prev, n = 0, 1
+    for w in widths:
+        parent += [first_prev] * w
+        first_prev, n = n, n + w
+    return np.array(parent, dtype=np.int64)
+
+
+def test_algorithmic_work_of_the_headline_workload():
+    """The roofline's numerator and byte count for 32 sequences, 64/8 heads,
+    head dim 128, prefix 8192 and the 65-position tree of widths
+    4/8/12/12/14/14: positions at depth d see d + 1 tree keys, so the tree
+    adds 1*1 + 4*2 + 8*3 + 12*4 + 12*5 + 14*6 + 14*7 = 323 visible pairs per
+    query head and sequence."""
+    import bench
+    B, Hq, Hkv, D, L, T = 32, 64, 8, 128, 8192, 65
+    parent = np.tile(_tree_from_widths([4, 8, 12, 12, 14, 14]), (B, 1))
+    inst = types.SimpleNamespace(B=B, Hq=Hq, Hkv=Hkv, D=D, T_max=T, dtype="bf16", parent=parent,
+                                 num_nodes=np.full(B, T), prefix_len=np.full(B, L))
+    flops, nbytes = bench.algorithmic_work(inst)
+    assert flops == 4 * Hq * D * B * (T * L + 323) == 558_684_438_528
+    # bf16: prefix K and V once, Q in and O out, the tree's K and V, one mask word per position
+    assert nbytes == 2 * (2 * B * Hkv * L * D + 2 * B * T * Hq * D + 2 * B * T * Hkv * D) + 8 * B * T * 2
+    assert nbytes == 1_150_452_224
+
+
+def test_algorithmic_work_counts_visible_pairs():
+    """Ragged sequences: the flop count is 4 * D per (query head, visible key)
+    pair, counted here pair by pair from the ancestor sets."""
+    import bench
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, D, T = 3, 4, 2, 64, 9
+    parent = np.full((B, T), -1, dtype=np.int64)
+    num_nodes = np.array([9, 1, 5])
+    for b in range(B):
+        for i in range(1, int(num_nodes[b])):
+            parent[b, i] = rng.integers(0, i)
+    prefix = np.array([100, 0, 7])
+    inst = types.SimpleNamespace(B=B, Hq=Hq, Hkv=Hkv, D=D, T_max=T, dtype="f32", parent=parent,
+                                 num_nodes=num_nodes, prefix_len=prefix)
+    pairs = 0
+    for b in range(B):
+        for i in range(int(num_nodes[b])):
+            seen, j = 0, i
+            while j >= 0:          # the node and its ancestors
+                seen += 1
+                j = int(parent[b, j])
+            pairs += int(prefix[b]) + seen
+    flops, _ = bench.algorithmic_work(inst)
+    assert flops == 4 * Hq * D * pairs
